@@ -1,0 +1,188 @@
+/*
+ * moe_route.h - C ABI of the MI355X (gfx950) group-limited MoE routing path.
+ *
+ * Three stages, each one entry point:
+ *   moe_router_group_limited  - group-limited top-k router
+ *   moe_create_indices        - bucket sort of routed slots into expert order
+ *   moe_finalize              - fused unpermute gather + weighted top-k sum
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory. Every tensor argument is a plain pointer to DEVICE memory owned by
+ * the caller, densely packed in row-major order (no strides). The library
+ * never allocates, frees or retains memory and keeps no state between calls.
+ * Scratch space, where needed, is a caller-provided device workspace.
+ *
+ * Streams. `stream` is a hipStream_t passed as void* (NULL = the legacy null
+ * stream of the current device). All work is enqueued asynchronously on that
+ * stream on the current HIP device; no call synchronises, copies to the host
+ * or reads device memory from the host, so every call can be captured into a
+ * HIP graph.
+ *
+ * Errors. Each call returns moe_status_t. Arguments are validated on the
+ * host before anything is enqueued; on any error nothing is launched and no
+ * output is written. MOE_ERR_HIP means a launch was rejected by the HIP
+ * runtime (moe_last_hip_error() gives the hipError_t value). Conditions on
+ * the *contents* of device buffers (expert ids in range, restore_order a
+ * permutation, finite scores) are preconditions, not checked: the kernels
+ * stay inside every buffer when they are violated, but the values written
+ * are then unspecified.
+ *
+ * Sizes are int64_t; T*K (the number of routed slots, N) must be below 2^32
+ * because all slot indices are uint32.
+ */
+#ifndef MOE_ROUTE_H
+#define MOE_ROUTE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1, /* size, shape or NULL pointer error */
+    MOE_ERR_UNSUPPORTED = 2, /* valid request this build has no kernel for */
+    MOE_ERR_ALIGNMENT = 3,   /* pointer or row size not 16-byte aligned */
+    MOE_ERR_WORKSPACE = 4,   /* workspace missing or too small */
+    MOE_ERR_HIP = 5          /* HIP runtime rejected a launch */
+} moe_status_t;
+
+typedef enum {
+    MOE_DTYPE_F32 = 0,  /* IEEE binary32 */
+    MOE_DTYPE_BF16 = 1  /* bfloat16 (high half of binary32) */
+} moe_dtype_t;
+
+/* How a group of experts is scored before the top-topk_group groups are
+ * kept. The router page says only that the groups "with the highest scores"
+ * survive; two readings are offered. */
+typedef enum {
+    MOE_GROUP_TOP2_SUM = 0, /* sum of the two largest biased scores in the group (default) */
+    MOE_GROUP_MAX = 1       /* largest biased score in the group */
+} moe_group_score_t;
+
+/*
+ * moe_router_group_limited
+ * Follows the group_limited_router_kernel page (Modular MAX Mojo API,
+ * nn/moe): description, Parameters and Args.
+ *
+ *   expert_indices   out int32 [T, K]: selected experts of each token.
+ *   expert_weights   out, dtype = scores_dtype, [T, K]: routing weights
+ *                    computed from the UNBIASED scores.
+ *   expert_scores    in  [T, E] routing scores, dtype scores_dtype.
+ *   expert_bias      in  [E] per-expert bias, dtype bias_dtype, added to the
+ *                    scores for selection only.
+ *   T                tokens (>= 0); E experts; K = experts per token.
+ *   n_groups         the E experts form n_groups consecutive groups of
+ *                    S = E / n_groups experts.
+ *   topk_group       number of best groups a token may select from.
+ *   norm_weights     non-zero: weights are divided by their sum over the K
+ *                    selected experts before scaling.
+ *   routed_scaling_factor  multiplied into every weight last.
+ *   group_score      see moe_group_score_t.
+ *
+ * Per token: b[e] = score[e] + bias[e] (fp32); groups ranked by group score
+ * (ties: lower group index first), the first topk_group kept; among their
+ * experts the K best by (b descending, expert index ascending) fill slots
+ * 0..K-1 in that order; weight_k = score[e_k] (/ sum) * scale in fp32.
+ *
+ * Validation: T >= 0; E >= 1 and E % n_groups == 0; 1 <= topk_group <=
+ * n_groups <= 64; 1 <= K <= topk_group * S; K <= 64; non-NULL pointers when
+ * T > 0. Supported: scores/bias F32; E a power of two, 1 <= E <= 1024
+ * (other E give MOE_ERR_UNSUPPORTED).
+ */
+moe_status_t moe_router_group_limited(int32_t* expert_indices, void* expert_weights,
+                                      const void* expert_scores, const void* expert_bias,
+                                      moe_dtype_t scores_dtype, moe_dtype_t bias_dtype,
+                                      int64_t T, int32_t E, int32_t K, int32_t n_groups,
+                                      int32_t topk_group, int32_t norm_weights,
+                                      float routed_scaling_factor, moe_group_score_t group_score,
+                                      void* stream);
+
+/*
+ * moe_create_indices_workspace_size
+ * Bytes of device workspace moe_create_indices needs for N slots and E
+ * experts (0 when none is needed). Pure host computation; never fails.
+ */
+size_t moe_create_indices_workspace_size(int64_t N, int32_t E);
+
+/*
+ * moe_create_indices
+ * Follows the moe_create_indices page (Modular MAX Mojo API, nn/moe):
+ * description (bucket sort grouping tokens by expert so each expert's
+ * tokens are contiguous) and Args.
+ *
+ *   token_expert_order    out uint32 [N]: slot indices i = t*K + k grouped
+ *                         by expert; experts ascending, and within an
+ *                         expert ascending i (stable).
+ *   expert_start_indices  out uint32 [E + 1]: CSR offsets of the active
+ *                         experts in token_expert_order; entry A (A = number
+ *                         of active experts) is N, entries after A are N.
+ *   restore_token_order   out uint32 [N]: position of slot i in
+ *                         token_expert_order (token_expert_order[restore[i]]
+ *                         == i).
+ *   expert_ids            out int32 [E]: active expert ids ascending, then -1.
+ *   expert_usage_stats    out uint32 [2]: {max slots on one expert, A}.
+ *   topk_ids              in int32 [N]: the router's [T, K] indices, flat.
+ *   N                     number of slots, 0 <= N < 2^32; E experts, 1..1024.
+ *   workspace             device buffer of at least
+ *                         moe_create_indices_workspace_size(N, E) bytes
+ *                         (may be NULL when that size is 0). Contents on
+ *                         entry do not matter; clobbered on exit.
+ *   scales_offset_p       must be NULL (aligned scale offsets for block-scaled
+ *                         grouped matmul are not produced by this build).
+ *
+ * Precondition: 0 <= topk_ids[i] < E. A slot whose id is out of range is left
+ * out of every count, its restore entry is set to 0xFFFFFFFF and the
+ * remaining outputs are unspecified but in bounds.
+ * Results are deterministic: no output depends on the order in which
+ * workgroups run.
+ */
+moe_status_t moe_create_indices(uint32_t* token_expert_order, uint32_t* expert_start_indices,
+                                uint32_t* restore_token_order, int32_t* expert_ids,
+                                uint32_t* expert_usage_stats, const int32_t* topk_ids,
+                                int64_t N, int32_t E, void* workspace, size_t workspace_bytes,
+                                uint32_t* scales_offset_p, void* stream);
+
+/*
+ * moe_finalize
+ * Follows the moe_finalize page (Modular MAX Mojo API, nn/moe): description
+ * (unpermute gather through restore_order, each row scaled by its router
+ * weight, fp32 accumulation, the [T, K, H] unpermuted tensor never formed)
+ * and Args.
+ *
+ *   output         out [T, H], out_dtype.
+ *   down           in [T*K, H], down_dtype: expert outputs in
+ *                  token_expert_order row order.
+ *   restore_order  in uint32 [T*K]: row of `down` for slot i = t*K + k.
+ *   router_weight  in [T, K], weight_dtype.
+ *
+ * output[t, h] = convert(sum_k w[t,k] * down[restore[t*K+k], h]) with the
+ * sum formed in fp32 from +0 by one fused multiply-add per k in ascending k;
+ * conversion to bf16 rounds to nearest even.
+ *
+ * Validation: T >= 0, K >= 1, H >= 0, T*K < 2^32; dtypes in {F32, BF16};
+ * H * sizeof(down_dtype) and H * sizeof(out_dtype) multiples of 16 bytes;
+ * output and down 16-byte aligned; non-NULL pointers when T*H > 0.
+ * Precondition: restore_order[i] < T*K (an out-of-range entry contributes
+ * nothing; the output is then unspecified but no access leaves `down`).
+ */
+moe_status_t moe_finalize(void* output, moe_dtype_t out_dtype, const void* down,
+                          moe_dtype_t down_dtype, const uint32_t* restore_order,
+                          const void* router_weight, moe_dtype_t weight_dtype, int64_t T,
+                          int32_t K, int64_t H, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* moe_status_string(moe_status_t status);
+
+/* hipError_t value behind the most recent MOE_ERR_HIP returned on this
+ * thread (0 if none). */
+int moe_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ROUTE_H */

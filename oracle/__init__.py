@@ -1,0 +1,159 @@
+"""CPU oracle for the group-limited MoE routing data path (ctypes wrapper).
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py`` may import this package. The
+product (``permutation_group_limited_amd``) never imports it, and the two
+share no code: the oracle is plain C in ``moe_oracle.c``, compiled with gcc
+(``-O2 -ffp-contract=off``, OpenMP across tokens only), and takes host numpy
+arrays.
+
+Conventions of this wrapper:
+  * bf16 arrays are passed and returned as ``numpy.uint16`` bit patterns;
+  * fp32 arrays as ``numpy.float32``; index arrays as int32 / uint32.
+
+Each function names the page passage it follows; the C file holds the
+step-by-step definitions and the readings of the pages' silent points.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
+
+F32 = 0
+BF16 = 1
+GROUP_TOP2_SUM = 0
+GROUP_MAX = 1
+_ERRORS = {1: "invalid argument", 2: "input violates a precondition", 3: "out of memory"}
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``moe_oracle.c`` into ``libmoe_oracle.so`` with gcc."""
+    global _lib
+    if not force and os.path.exists(_LIB_PATH):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+           "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    _lib = None
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        p = ctypes.c_void_p
+        i32, i64 = ctypes.c_int32, ctypes.c_int64
+        lib.moe_oracle_router.argtypes = [p, p, p, p, i64, i32, i32, i32, i32, i32,
+                                          ctypes.c_float, i32]
+        lib.moe_oracle_router.restype = ctypes.c_int
+        lib.moe_oracle_create_indices.argtypes = [p, p, p, p, p, p, i64, i32]
+        lib.moe_oracle_create_indices.restype = ctypes.c_int
+        lib.moe_oracle_finalize.argtypes = [p, i32, p, i32, p, p, i32, i64, i32, i64]
+        lib.moe_oracle_finalize.restype = ctypes.c_int
+        lib.moe_oracle_f32_to_bf16_array.argtypes = [p, p, i64]
+        lib.moe_oracle_f32_to_bf16_array.restype = None
+        lib.moe_oracle_num_threads.argtypes = []
+        lib.moe_oracle_num_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise ValueError("oracle %s: %s" % (what, _ERRORS.get(rc, "error %d" % rc)))
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().moe_oracle_num_threads())
+
+
+def router(scores, bias, k: int, n_groups: int, topk_group: int, norm_weights: bool,
+           routed_scaling_factor: float, group_score: int = GROUP_TOP2_SUM):
+    """Group-limited top-k router (group_limited_router_kernel page, description,
+    Parameters and Args). Returns (expert_indices int32 [T, K],
+    expert_weights float32 [T, K])."""
+    s = np.ascontiguousarray(scores, dtype=np.float32)
+    b = np.ascontiguousarray(bias, dtype=np.float32)
+    T, E = s.shape
+    assert b.shape == (E,)
+    idx = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float32)
+    rc = _load().moe_oracle_router(_ptr(idx), _ptr(w), _ptr(s), _ptr(b), T, E, k, n_groups,
+                                   topk_group, int(bool(norm_weights)),
+                                   ctypes.c_float(routed_scaling_factor), group_score)
+    _check(rc, "router")
+    return idx, w
+
+
+def create_indices(topk_ids, n_experts: int):
+    """Bucket sort of routed slots by expert (moe_create_indices page, description
+    and Args). Returns a dict with token_expert_order, expert_start_indices,
+    restore_token_order (uint32), expert_ids (int32), expert_usage_stats (uint32)."""
+    ids = np.ascontiguousarray(topk_ids, dtype=np.int32).reshape(-1)
+    n = ids.shape[0]
+    out = {
+        "token_expert_order": np.empty(n, dtype=np.uint32),
+        "expert_start_indices": np.empty(n_experts + 1, dtype=np.uint32),
+        "restore_token_order": np.empty(n, dtype=np.uint32),
+        "expert_ids": np.empty(n_experts, dtype=np.int32),
+        "expert_usage_stats": np.empty(2, dtype=np.uint32),
+    }
+    rc = _load().moe_oracle_create_indices(
+        _ptr(out["token_expert_order"]), _ptr(out["expert_start_indices"]),
+        _ptr(out["restore_token_order"]), _ptr(out["expert_ids"]),
+        _ptr(out["expert_usage_stats"]), _ptr(ids), n, n_experts)
+    _check(rc, "create_indices")
+    return out
+
+
+def finalize(down, down_dtype: int, restore_order, router_weight, weight_dtype: int,
+             out_dtype: int):
+    """Fused unpermute gather plus weighted top-k sum (moe_finalize page,
+    description and Args). ``down`` is [T*K, H] (float32, or uint16 bf16 bits),
+    ``router_weight`` is [T, K]. Returns [T, H] float32 or uint16 bf16 bits."""
+    d = np.ascontiguousarray(down)
+    w = np.ascontiguousarray(router_weight)
+    r = np.ascontiguousarray(restore_order, dtype=np.uint32).reshape(-1)
+    assert d.dtype == (np.float32 if down_dtype == F32 else np.uint16)
+    assert w.dtype == (np.float32 if weight_dtype == F32 else np.uint16)
+    T, K = w.shape
+    N, H = d.shape
+    assert N == T * K and r.shape[0] == N
+    out = np.empty((T, H), dtype=np.float32 if out_dtype == F32 else np.uint16)
+    rc = _load().moe_oracle_finalize(_ptr(out), out_dtype, _ptr(d), down_dtype, _ptr(r), _ptr(w),
+                                     weight_dtype, T, K, H)
+    _check(rc, "finalize")
+    return out
+
+
+def f32_to_bf16(x) -> np.ndarray:
+    """Round binary32 values to bf16 (nearest, ties to even); uint16 bits."""
+    a = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(a.shape, dtype=np.uint16)
+    _load().moe_oracle_f32_to_bf16_array(_ptr(out), _ptr(a), a.size)
+    return out
+
+
+def bf16_to_f32(bits) -> np.ndarray:
+    """Widen bf16 bit patterns to float32 (exact)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
