@@ -1,0 +1,272 @@
+"""Benchmark of the routing path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3]
+
+One step = one pass of the whole path over one batch: router ->
+create_indices -> finalize, all through the C ABI on torch's current
+stream, with every input already resident in HBM. W untimed steps, then K
+timed steps between a synchronize and HIP events; prints ONE JSON line.
+
+Headline workload: DeepSeek-V3-shaped, T=8192 tokens, E=256 experts in 8
+groups (4 kept), K=8, hidden 7168, bf16 expert outputs and output. One
+routed token-slot is one (token, k) pair, i.e. one row of `down`.
+
+Reported beside the throughput:
+  * roofline of the dominant kernel (finalize): algorithmic bytes per launch
+    (T*K*H*2 read + T*K*(4+4) restore and weights + T*H*2 written) divided by
+    its mean duration from HIP events recorded around each finalize launch
+    on the launch stream inside the timed region, against 8 TB/s; plus the
+    HBM bytes measured by rocprofv3 counters when the committed counter
+    summary matches the current kernel source;
+  * cpu_baseline: the CPU oracle (plain C, OpenMP over tokens) timed on the
+    host cores over whole steps of the same workload, and a parity check of
+    the GPU step against it.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, vendor figure
+COUNTER_FILE = os.path.join(ROOT, "profiles", "finalize_dsv3_counters.txt")
+FINALIZE_SOURCES = [os.path.join(ROOT, "permutation_group_limited_amd", "csrc", f)
+                    for f in ("finalize.hip", "common.hpp")]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="approximate CPU time for the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def finalize_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in FINALIZE_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counter_traffic():
+    """HBM bytes per finalize launch from the committed rocprofv3 counter
+    summary, or None if it is missing or was taken on other kernel source."""
+    try:
+        with open(COUNTER_FILE) as f:
+            kv = dict(l.split(":", 1) for l in f if ":" in l and not l.startswith("#"))
+        kv = {k.strip(): v.strip() for k, v in kv.items()}
+        if kv.get("kernel_source_sha256") != finalize_source_hash():
+            return None
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the routing path "
+              "shards by token with no exchange; run one process per GPU). --gpus %d refused."
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from permutation_group_limited_amd import binding
+    from permutation_group_limited_amd import workloads as wl
+
+    binding.load_library()  # raises if the HIP library is not built
+    wk = wl.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    T, E, K, H = wk.T, wk.E, wk.K, wk.H
+    N = T * K
+    db = 2 if wk.down_dtype == torch.bfloat16 else 4
+    ob = 2 if wk.out_dtype == torch.bfloat16 else 4
+
+    scores_h, bias_h = wl.make_scores(wk), wl.make_bias(wk)
+    scores, bias = scores_h.to(dev), bias_h.to(dev)
+    down = wl.make_down(wk, device=dev)
+    idx = torch.empty(T, K, dtype=torch.int32, device=dev)
+    wts = torch.empty(T, K, dtype=torch.float32, device=dev)
+    order = torch.empty(N, dtype=torch.int32, device=dev)
+    restore = torch.empty(N, dtype=torch.int32, device=dev)
+    starts = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    eids = torch.empty(E, dtype=torch.int32, device=dev)
+    stats = torch.empty(2, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(binding.moe_create_indices_workspace_size(N, E), 4) // 4,
+                     dtype=torch.int32, device=dev)
+    out = torch.empty(T, H, dtype=wk.out_dtype, device=dev)
+
+    def step(ev=None):
+        binding.moe_router_group_limited(idx, wts, scores, bias, wk.n_groups, wk.topk_group,
+                                         wk.norm_weights, wk.scale)
+        binding.moe_create_indices(order, starts, restore, eids, stats, idx, ws)
+        if ev is not None:
+            ev[0].record()
+        binding.moe_finalize(out, down, restore, wts)
+        if ev is not None:
+            ev[1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    fin_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        step(fin_ev[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    elapsed_ms = t_start.elapsed_time(t_end)
+    fin_ms = [a.elapsed_time(b) for a, b in fin_ev]
+    ms_per_step = elapsed_ms / args.steps
+    fin_avg_ms = sum(fin_ms) / len(fin_ms)
+
+    bytes_router = T * E * 4 + E * 4 + N * (4 + 4)
+    bytes_indices = N * 4 + 2 * N * 4 + (2 * E + 1) * 4 + 8
+    bytes_finalize = N * H * db + N * (4 + 4) + T * H * ob
+    bytes_total = bytes_router + bytes_indices + bytes_finalize
+    step_s = ms_per_step * 1e-3
+    fin_gbps = bytes_finalize / (fin_avg_ms * 1e-3) / 1e9
+    traffic = counter_traffic()
+
+    result = {
+        "metric": "routed token-slots/s + HBM GB/s (% of peak), DSv3 shape T=8192 E=256 K=8",
+        "value": N / step_s,
+        "unit": "token-slots/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; sigmoid/softmax scores, N(0,1) expert outputs)",
+        "config": {"workload": wk.describe(), "tokens": T, "experts": E, "n_groups": wk.n_groups,
+                   "topk_group": wk.topk_group, "top_k": K, "hidden": H,
+                   "storage": "bf16" if db == 2 else "f32", "accumulate": "f32"},
+        "hbm_gbps": bytes_total / step_s / 1e9,
+        "hbm_pct_of_peak": 100.0 * bytes_total / step_s / 1e9 / PEAK_HBM_GBPS,
+        "algorithmic_bytes_per_step": bytes_total,
+        "stage_bytes": {"router": bytes_router, "create_indices": bytes_indices,
+                        "finalize": bytes_finalize},
+        "finalize_ms": fin_avg_ms,
+        "wall_s": wall,
+        "roofline": {"kernel": "finalize_kernel", "bound": "hbm", "achieved": fin_gbps,
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": fin_gbps / PEAK_HBM_GBPS,
+                     "traffic": traffic},
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"], result["parity"] = cpu_leg(
+            wk, scores_h, bias_h, down, idx, wts, order, restore, starts, eids, stats, out,
+            args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_leg(wk, scores_h, bias_h, down, idx, wts, order, restore, starts, eids, stats, out,
+            budget_s):
+    """Time the CPU oracle over whole steps of the same workload and check the
+    GPU step against it."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    T, E, K = wk.T, wk.E, wk.K
+    N = T * K
+    s = scores_h.numpy()
+    b = bias_h.numpy()
+    if wk.down_dtype == torch.bfloat16:
+        d = down.cpu().view(torch.int16).numpy().view(np.uint16)
+        dcode = oracle.BF16
+    else:
+        d = down.cpu().numpy()
+        dcode = oracle.F32
+    ocode = oracle.BF16 if wk.out_dtype == torch.bfloat16 else oracle.F32
+
+    def oracle_step():
+        oi, ow = oracle.router(s, b, K, wk.n_groups, wk.topk_group, wk.norm_weights, wk.scale)
+        ind = oracle.create_indices(oi, E)
+        o = oracle.finalize(d, dcode, ind["restore_token_order"], ow, oracle.F32, ocode)
+        return oi, ow, ind, o
+
+    steps = 0
+    t0 = time.perf_counter()
+    res = None
+    while True:
+        res = oracle_step()
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or steps >= 200:
+            break
+    oi, ow, ind, o = res
+    baseline = {"value": N * steps / el, "unit": "token-slots/s", "cores": oracle.num_threads(),
+                "kind": "oracle",
+                "sample": "%d whole steps of the %s workload (router + create_indices + "
+                          "finalize), %.1f s" % (steps, wk.name, el)}
+
+    u32 = lambda t: t.cpu().numpy().view(np.uint32)
+    gi = idx.cpu().numpy()
+    gw = wts.cpu().numpy()
+    parity = {
+        "router_indices": bool(np.array_equal(gi, oi)),
+        "router_weights": bool(np.all(np.abs(gw.astype(np.float64) - ow) <=
+                                      1e-6 * np.abs(ow.astype(np.float64)))),
+        "create_indices": bool(np.array_equal(u32(order), ind["token_expert_order"]) and
+                               np.array_equal(u32(restore), ind["restore_token_order"]) and
+                               np.array_equal(u32(starts), ind["expert_start_indices"]) and
+                               np.array_equal(eids.cpu().numpy(), ind["expert_ids"]) and
+                               np.array_equal(u32(stats), ind["expert_usage_stats"])),
+    }
+    # finalize ran on the GPU's own weights (within 1e-6 of the oracle's):
+    # accept 1 bf16 ulp, or (1e-6 + 2*K*2^-24) * sum|w*d| plus one spacing
+    if ocode == oracle.BF16:
+        gb = out.cpu().view(torch.int16).numpy().view(np.uint16)
+        g = oracle.bf16_to_f32(gb).astype(np.float64)
+        e = oracle.bf16_to_f32(o).astype(np.float64)
+        ordg = np.where(gb & 0x8000, -(gb.astype(np.int64) & 0x7FFF), gb & 0x7FFF)
+        orde = np.where(o & 0x8000, -(o.astype(np.int64) & 0x7FFF), o & 0x7FFF)
+        ulp = np.abs(ordg - orde)
+        parity["finalize_max_ulp"] = int(ulp.max())
+        bad = ulp > 1
+        if bad.any():
+            rows_bad = np.unique(np.nonzero(bad)[0])
+            rsel = ind["restore_token_order"].reshape(T, K)[rows_bad].astype(np.int64)
+            dd = oracle.bf16_to_f32(d[rsel.reshape(-1)]).astype(np.float64).reshape(
+                rows_bad.size, K, -1)
+            mag = (np.abs(ow[rows_bad].astype(np.float64))[:, :, None] * np.abs(dd)).sum(1)
+            top = np.maximum(np.abs(g[rows_bad]), np.abs(e[rows_bad]))
+            spacing = np.exp2(np.floor(np.log2(np.where(top > 0, top, 1.0))) - 7.0)
+            within = np.abs(g[rows_bad] - e[rows_bad]) <= \
+                (1e-6 + 2 * K * 2.0 ** -24) * mag + spacing
+            bad[rows_bad] &= ~within
+        parity["finalize"] = not bool(bad.any())
+    else:
+        parity["finalize"] = bool(np.allclose(out.cpu().numpy(), o, rtol=1e-5, atol=1e-6))
+    return baseline, parity
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,126 @@
+// C ABI of the routing path: argument validation, then one launcher per
+// stage on the caller's stream. Nothing here allocates, synchronises or
+// touches device memory from the host.
+#include <limits.h>
+
+#include "common.hpp"
+
+namespace moe {
+namespace {
+thread_local int g_last_hip_error = 0;
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+size_t dtype_bytes(moe_dtype_t d) { return d == MOE_DTYPE_F32 ? 4 : 2; }
+bool dtype_ok(moe_dtype_t d) { return d == MOE_DTYPE_F32 || d == MOE_DTYPE_BF16; }
+}  // namespace
+
+moe_status_t hip_failure(hipError_t err) {
+  g_last_hip_error = static_cast<int>(err);
+  return MOE_ERR_HIP;
+}
+
+moe_status_t check_launch() {
+  const hipError_t err = hipGetLastError();
+  return err == hipSuccess ? MOE_OK : hip_failure(err);
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+moe_status_t moe_router_group_limited(int32_t* expert_indices, void* expert_weights,
+                                      const void* expert_scores, const void* expert_bias,
+                                      moe_dtype_t scores_dtype, moe_dtype_t bias_dtype,
+                                      int64_t T, int32_t E, int32_t K, int32_t n_groups,
+                                      int32_t topk_group, int32_t norm_weights,
+                                      float routed_scaling_factor, moe_group_score_t group_score,
+                                      void* stream) {
+  if (T < 0 || E < 1 || n_groups < 1 || n_groups > 64 || E % n_groups != 0)
+    return MOE_ERR_INVALID_ARG;
+  if (topk_group < 1 || topk_group > n_groups) return MOE_ERR_INVALID_ARG;
+  const int64_t S = E / n_groups;
+  if (K < 1 || K > topk_group * S || K > 64) return MOE_ERR_INVALID_ARG;
+  if (group_score != MOE_GROUP_TOP2_SUM && group_score != MOE_GROUP_MAX)
+    return MOE_ERR_INVALID_ARG;
+  if (!dtype_ok(scores_dtype) || !dtype_ok(bias_dtype)) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!expert_indices || !expert_weights || !expert_scores || !expert_bias))
+    return MOE_ERR_INVALID_ARG;
+  if (T > (int64_t)UINT32_MAX / K) return MOE_ERR_INVALID_ARG;
+  if (scores_dtype != MOE_DTYPE_F32 || bias_dtype != MOE_DTYPE_F32) return MOE_ERR_UNSUPPORTED;
+  if (!is_pow2(E) || E > 1024) return MOE_ERR_UNSUPPORTED;
+  if (!aligned(expert_scores, 16) || !aligned(expert_bias, 16) || !aligned(expert_indices, 4) ||
+      !aligned(expert_weights, 4))
+    return MOE_ERR_ALIGNMENT;
+  if (T == 0) return MOE_OK;
+  return launch_router(expert_indices, static_cast<float*>(expert_weights),
+                       static_cast<const float*>(expert_scores),
+                       static_cast<const float*>(expert_bias), T, E, K, n_groups, topk_group,
+                       norm_weights ? 1 : 0, routed_scaling_factor,
+                       static_cast<int32_t>(group_score), static_cast<hipStream_t>(stream));
+}
+
+size_t moe_create_indices_workspace_size(int64_t N, int32_t E) {
+  if (N < 0 || E < 1) return 0;
+  return plan_indices(N, E).workspace_bytes;
+}
+
+moe_status_t moe_create_indices(uint32_t* token_expert_order, uint32_t* expert_start_indices,
+                                uint32_t* restore_token_order, int32_t* expert_ids,
+                                uint32_t* expert_usage_stats, const int32_t* topk_ids,
+                                int64_t N, int32_t E, void* workspace, size_t workspace_bytes,
+                                uint32_t* scales_offset_p, void* stream) {
+  if (N < 0 || N > (int64_t)UINT32_MAX || E < 1 || E > 1024) return MOE_ERR_INVALID_ARG;
+  if (!expert_start_indices || !expert_ids || !expert_usage_stats) return MOE_ERR_INVALID_ARG;
+  if (N > 0 && (!token_expert_order || !restore_token_order || !topk_ids))
+    return MOE_ERR_INVALID_ARG;
+  if (scales_offset_p != nullptr) return MOE_ERR_UNSUPPORTED;
+  const IndexPlan plan = plan_indices(N, E);
+  if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
+    return MOE_ERR_WORKSPACE;
+  if (!aligned(workspace, 4) || !aligned(token_expert_order, 4) ||
+      !aligned(expert_start_indices, 4) || !aligned(restore_token_order, 4) ||
+      !aligned(expert_ids, 4) || !aligned(expert_usage_stats, 4) || !aligned(topk_ids, 4))
+    return MOE_ERR_ALIGNMENT;
+  return launch_indices(token_expert_order, expert_start_indices, restore_token_order, expert_ids,
+                        expert_usage_stats, topk_ids, N, E, workspace, plan,
+                        static_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_finalize(void* output, moe_dtype_t out_dtype, const void* down,
+                          moe_dtype_t down_dtype, const uint32_t* restore_order,
+                          const void* router_weight, moe_dtype_t weight_dtype, int64_t T,
+                          int32_t K, int64_t H, void* stream) {
+  if (T < 0 || K < 1 || H < 0) return MOE_ERR_INVALID_ARG;
+  if (!dtype_ok(out_dtype) || !dtype_ok(down_dtype) || !dtype_ok(weight_dtype))
+    return MOE_ERR_INVALID_ARG;
+  if (T > (int64_t)UINT32_MAX / K) return MOE_ERR_INVALID_ARG;
+  if (H > ((int64_t)1 << 40)) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && H > 0 && (!output || !down || !restore_order || !router_weight))
+    return MOE_ERR_INVALID_ARG;
+  if ((H * static_cast<int64_t>(dtype_bytes(down_dtype))) % 16 != 0) return MOE_ERR_ALIGNMENT;
+  if (!aligned(output, 16) || !aligned(down, 16) || !aligned(restore_order, 4) ||
+      !aligned(router_weight, dtype_bytes(weight_dtype)))
+    return MOE_ERR_ALIGNMENT;
+  if (T == 0 || H == 0) return MOE_OK;
+  return launch_finalize(output, out_dtype, down, down_dtype, restore_order, router_weight,
+                         weight_dtype, T, K, H, static_cast<hipStream_t>(stream));
+}
+
+const char* moe_status_string(moe_status_t status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_ALIGNMENT: return "misaligned pointer or row size";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int moe_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

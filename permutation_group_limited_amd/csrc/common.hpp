@@ -1,0 +1,98 @@
+// Device helpers shared by the gfx950 kernels of the routing path.
+//
+// Everything here is CDNA wave64 code: 64-lane wavefronts, 64-bit ballots,
+// cross-lane traffic through ds_bpermute / DPP (via the HIP shuffle
+// intrinsics), bf16 conversion by the gfx950 hardware converter
+// (v_cvt_pk_bf16_f32, round to nearest even).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_route.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;  // 4 waves per workgroup for every kernel
+constexpr int kWavesPerBlock = kBlock / kWave;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (hardware conversion on gfx950).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  __bf16 b = static_cast<__bf16>(f);
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b));
+}
+
+// Monotone map binary32 -> uint32 for finite inputs: a < b  <=>  key(a) <
+// key(b), and -0 / +0 map to the same key (IEEE equality).
+__device__ __forceinline__ uint32_t ordered_key(float v) {
+  uint32_t u = __float_as_uint(v);
+  if (v == 0.0f) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
+  uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
+  lo = static_cast<uint32_t>(__shfl_xor(static_cast<int>(lo), mask, kWave));
+  hi = static_cast<uint32_t>(__shfl_xor(static_cast<int>(hi), mask, kWave));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x) & (kWave - 1); }
+
+// Number of set bits of `mask` in lanes below the calling lane.
+__device__ __forceinline__ uint32_t popc_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
+}
+
+// Lanes of the wave whose `key` equals the caller's, restricted to `active`
+// (a 64-bit ballot per key bit; `nbits` covers every key in use).
+__device__ __forceinline__ uint64_t match_any(uint32_t key, int nbits, uint64_t active) {
+  uint64_t peers = active;
+  for (int bit = 0; bit < nbits; ++bit) {
+    const bool set = (key >> bit) & 1u;
+    const uint64_t bal = __ballot(set);
+    peers &= set ? bal : ~bal;
+  }
+  return peers;
+}
+
+// ---- launchers (host side), one per stage --------------------------------
+
+moe_status_t launch_router(int32_t* expert_indices, float* expert_weights, const float* scores,
+                           const float* bias, int64_t T, int32_t E, int32_t K, int32_t n_groups,
+                           int32_t topk_group, int32_t norm_weights, float scale, int32_t mode,
+                           hipStream_t stream);
+
+struct IndexPlan {
+  int64_t chunk;    // slots per workgroup
+  int64_t nchunks;  // workgroups of the scatter (and histogram) launch
+  int rounds;       // 64-slot rounds per wave
+  size_t workspace_bytes;
+};
+IndexPlan plan_indices(int64_t N, int32_t E);
+
+moe_status_t launch_indices(uint32_t* token_expert_order, uint32_t* expert_start_indices,
+                            uint32_t* restore_token_order, int32_t* expert_ids,
+                            uint32_t* expert_usage_stats, const int32_t* topk_ids, int64_t N,
+                            int32_t E, void* workspace, const IndexPlan& plan, hipStream_t stream);
+
+moe_status_t launch_finalize(void* output, moe_dtype_t out_dtype, const void* down,
+                             moe_dtype_t down_dtype, const uint32_t* restore_order,
+                             const void* router_weight, moe_dtype_t weight_dtype, int64_t T,
+                             int32_t K, int64_t H, hipStream_t stream);
+
+// Records the HIP error of a failed launch for moe_last_hip_error().
+moe_status_t hip_failure(hipError_t err);
+moe_status_t check_launch();
+
+}  // namespace moe

@@ -1,0 +1,171 @@
+"""Helpers shared by the GPU parity tests: run one stage of the HIP library
+through the C ABI on host inputs, and the acceptance comparisons.
+
+Acceptance:
+  * expert indices, token_expert_order, restore_token_order,
+    expert_start_indices, expert_ids, expert_usage_stats: bit-exact;
+  * router weights: |gpu - oracle| <= 1e-6 * |oracle|;
+  * finalize, fp32 output: |gpu - oracle| <= 1e-5 * sum_k |w_k * down_k|
+    (relative to the magnitude of the terms, so cancellation cannot fail a
+    correct result);
+  * finalize, bf16 output: at most 1 bf16 ulp apart (ordered bit patterns,
+    +0 and -0 equal);
+  * the chained pipeline feeds finalize the GPU's own weights, which may
+    differ from the oracle's within the router tolerance (1e-6 relative);
+    there the bound is (1e-6 + 2*K*2^-24) * sum_k |w_k d_k| (that weight
+    difference plus the error of two K-term fp32 chains) plus one bf16
+    spacing for the two final roundings.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from permutation_group_limited_amd import binding
+
+DEV = "cuda:0"
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_np_u32(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().view(torch.int32).numpy().view(np.uint32)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def gpu_router(scores, bias, K, G, TG, norm, scale, mode=0):
+    T, E = scores.shape
+    s = scores.to(DEV)
+    b = bias.to(DEV)
+    idx = torch.full((T, K), -7, dtype=torch.int32, device=DEV)
+    w = torch.full((T, K), float("nan"), dtype=torch.float32, device=DEV)
+    binding.moe_router_group_limited(idx, w, s, b, G, TG, norm, scale, mode)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), w.cpu().numpy()
+
+
+def gpu_indices(ids, E, poison=True):
+    ids = torch.as_tensor(ids).reshape(-1).to(torch.int32)
+    n = ids.numel()
+    d = ids.to(DEV)
+    fill = 0x5A5A5A5A if poison else 0
+    order = torch.full((n,), fill, dtype=torch.int32, device=DEV)
+    restore = torch.full((n,), fill, dtype=torch.int32, device=DEV)
+    starts = torch.full((E + 1,), fill, dtype=torch.int32, device=DEV)
+    eids = torch.full((E,), fill, dtype=torch.int32, device=DEV)
+    stats = torch.full((2,), fill, dtype=torch.int32, device=DEV)
+    ws_bytes = binding.moe_create_indices_workspace_size(n, E)
+    ws = torch.full((max(ws_bytes, 4) // 4,), fill, dtype=torch.int32, device=DEV)
+    binding.moe_create_indices(order, starts, restore, eids, stats, d, ws)
+    torch.cuda.synchronize()
+    return {
+        "token_expert_order": to_np_u32(order),
+        "expert_start_indices": to_np_u32(starts),
+        "restore_token_order": to_np_u32(restore),
+        "expert_ids": eids.cpu().numpy(),
+        "expert_usage_stats": to_np_u32(stats),
+    }
+
+
+def gpu_finalize(down_dev, restore, weight, out_dtype):
+    T, K = weight.shape
+    H = down_dev.shape[1]
+    r = torch.as_tensor(np.asarray(restore, dtype=np.uint32).view(np.int32)).to(DEV)
+    w = weight.to(DEV)
+    out = torch.full((T, H), float("nan"), dtype=out_dtype, device=DEV)
+    binding.moe_finalize(out, down_dev, r, w)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_finalize_from(down_host, restore, weight, out_dtype):
+    """Oracle finalize on host tensors (down/weight float32 or bfloat16)."""
+    def enc(t):
+        if t.dtype == torch.bfloat16:
+            return bf16_bits(t), oracle.BF16
+        return t.contiguous().numpy(), oracle.F32
+    d, dd = enc(down_host)
+    w, wd = enc(weight)
+    od = oracle.BF16 if out_dtype == torch.bfloat16 else oracle.F32
+    return oracle.finalize(d, dd, np.asarray(restore, dtype=np.uint32), w, wd, od)
+
+
+def term_magnitude(down_host, restore, weight):
+    """sum_k |w_k * down[restore[t*K+k]]| in float64, [T, H]."""
+    T, K = weight.shape
+    d = down_host.to(torch.float64)
+    rows = d[torch.as_tensor(np.asarray(restore, dtype=np.int64))].reshape(T, K, -1)
+    return (weight.to(torch.float64).abs()[:, :, None] * rows.abs()).sum(1).numpy()
+
+
+def assert_indices_equal(got, exp):
+    for key in ("token_expert_order", "expert_start_indices", "restore_token_order",
+                "expert_ids", "expert_usage_stats"):
+        g, e = np.asarray(got[key]), np.asarray(exp[key])
+        if not np.array_equal(g, e):
+            bad = np.nonzero(g.reshape(-1) != e.reshape(-1))[0]
+            raise AssertionError("%s differs at %d places, first %s: gpu %s oracle %s"
+                                 % (key, bad.size, bad[:5], g.reshape(-1)[bad[:5]],
+                                    e.reshape(-1)[bad[:5]]))
+
+
+def assert_weights_close(got, exp):
+    got = np.asarray(got, np.float64)
+    exp = np.asarray(exp, np.float64)
+    err = np.abs(got - exp)
+    ok = err <= 1e-6 * np.abs(exp)
+    if not np.all(ok):
+        i = np.argwhere(~ok)[:5]
+        raise AssertionError("weights beyond 1e-6 relative at %s: gpu %s oracle %s"
+                             % (i.tolist(), got[tuple(i.T)], exp[tuple(i.T)]))
+
+
+def _bf16_ordered(bits: np.ndarray) -> np.ndarray:
+    b = bits.astype(np.int64)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def bf16_spacing(x: np.ndarray) -> np.ndarray:
+    """Distance from |x| to the next bf16 value away from zero (x in float64)."""
+    a = np.abs(x)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, np.exp2(np.maximum(e, -126.0) - 7.0), 2.0 ** -133)
+
+
+def assert_finalize_close(got_dev, exp_np, mag, weight_rel_tol=0.0):
+    """Finalize acceptance. With weight_rel_tol > 0 (the chained pipeline,
+    where the GPU's weights may differ from the oracle's by the router's
+    tolerance) an output also passes when it is within weight_rel_tol *
+    sum_k |w_k d_k| plus one bf16 spacing of the oracle's."""
+    if got_dev.dtype == torch.bfloat16:
+        gb, eb = bf16_bits(got_dev), np.asarray(exp_np, np.uint16)
+        diff = np.abs(_bf16_ordered(gb) - _bf16_ordered(eb))
+        bad = diff > 1
+        if weight_rel_tol > 0 and bad.any():
+            gf = oracle.bf16_to_f32(gb).astype(np.float64)
+            ef = oracle.bf16_to_f32(eb).astype(np.float64)
+            spacing = bf16_spacing(np.maximum(np.abs(gf), np.abs(ef)))
+            bad &= np.abs(gf - ef) > weight_rel_tol * mag + spacing
+        if bad.any():
+            i = np.argwhere(bad)[:5]
+            raise AssertionError("bf16 output beyond tolerance at %s" % i.tolist())
+        return int(diff.max(initial=0))
+    g = got_dev.cpu().numpy().astype(np.float64)
+    e = np.asarray(exp_np, np.float64)
+    err = np.abs(g - e)
+    ok = err <= (1e-5 + weight_rel_tol) * mag
+    if not np.all(ok):
+        i = np.argwhere(~ok)[:5]
+        raise AssertionError("fp32 output beyond 1e-5 of the term magnitude at %s"
+                             % i.tolist())
+    return float(err.max(initial=0.0))

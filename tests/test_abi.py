@@ -1,0 +1,125 @@
+"""The C-ABI library: it loads, exports every entry point that
+include/moe_route.h declares, and rejects bad arguments on the host before
+any launch (these calls never reach the GPU, so they run on the CPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch  # noqa: F401  (the binding must share torch's HIP runtime)
+
+from permutation_group_limited_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_route.h")
+
+OK, INVALID, UNSUPPORTED, ALIGNMENT, WORKSPACE = 0, 1, 2, 3, 4
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.library_path()):
+        from permutation_group_limited_amd import build
+        build.build()
+    return binding.load_library()
+
+
+def test_header_declares_the_three_stages():
+    names = declared_functions()
+    for fn in ("moe_router_group_limited", "moe_create_indices",
+               "moe_create_indices_workspace_size", "moe_finalize"):
+        assert fn in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for fn in declared_functions():
+        assert hasattr(lib, fn), fn
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        assert lib.moe_status_string(code)
+    assert lib.moe_last_hip_error() == 0
+
+
+P = ctypes.c_void_p
+FAKE = P(0x10000)  # 16-byte aligned, never dereferenced: validation fails first
+FAKE_MIS = P(0x10004)
+FAKE_ODD = P(0x10002)
+
+
+def router(lib, T=4, E=256, K=8, G=8, TG=4, norm=1, mode=0, ptrs=None, sd=0, bd=0):
+    p = ptrs or (FAKE, FAKE, FAKE, FAKE)
+    return lib.moe_router_group_limited(p[0], p[1], p[2], p[3], sd, bd, T, E, K, G, TG, norm,
+                                        ctypes.c_float(1.0), mode, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), INVALID), (dict(E=0), INVALID), (dict(G=3), INVALID),
+    (dict(G=128, E=256, TG=4), INVALID), (dict(TG=0), INVALID), (dict(TG=9), INVALID),
+    (dict(K=0), INVALID), (dict(K=129, TG=4), INVALID), (dict(E=256, G=8, TG=1, K=33), INVALID),
+    (dict(E=1024, G=1, TG=1, K=65), INVALID), (dict(mode=2), INVALID), (dict(sd=7), INVALID),
+    (dict(sd=1), UNSUPPORTED), (dict(bd=1), UNSUPPORTED), (dict(E=96, G=8, TG=4), UNSUPPORTED),
+    (dict(E=2048, G=8, TG=4), UNSUPPORTED),
+    (dict(ptrs=(None, FAKE, FAKE, FAKE)), INVALID),
+    (dict(ptrs=(FAKE, FAKE, FAKE_MIS, FAKE)), ALIGNMENT),
+    (dict(T=0, ptrs=(None, None, None, None)), OK),
+])
+def test_router_validation(lib, kw, code):
+    assert router(lib, **kw) == code
+
+
+def indices(lib, N=1000, E=256, ws=None, ws_bytes=1 << 20, scales=None, ptrs=None):
+    p = ptrs or (FAKE,) * 6
+    return lib.moe_create_indices(p[0], p[1], p[2], p[3], p[4], p[5], N, E,
+                                  FAKE if ws is None else ws, ws_bytes, scales, None)
+
+
+def test_workspace_size(lib):
+    assert lib.moe_create_indices_workspace_size(0, 256) == 0
+    assert lib.moe_create_indices_workspace_size(1024, 256) == 0  # one chunk: no workspace
+    big = lib.moe_create_indices_workspace_size(524288, 256)
+    assert big >= 256 * 4 and big % 4 == 0
+    assert lib.moe_create_indices_workspace_size(-1, 256) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=-1), INVALID), (dict(N=1 << 32), INVALID), (dict(E=0), INVALID),
+    (dict(E=1025), INVALID), (dict(scales=FAKE), UNSUPPORTED),
+    (dict(N=65536, ws_bytes=16), WORKSPACE),
+    (dict(ptrs=(None,) + (FAKE,) * 5), INVALID),
+    (dict(ptrs=(FAKE_ODD,) + (FAKE,) * 5, N=100), ALIGNMENT),
+])
+def test_indices_validation(lib, kw, code):
+    assert indices(lib, **kw) == code
+
+
+def finalize(lib, T=4, K=2, H=64, od=1, dd=1, wd=0, ptrs=None):
+    p = ptrs or (FAKE,) * 4
+    return lib.moe_finalize(p[0], od, p[1], dd, p[2], p[3], wd, T, K, H, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), INVALID), (dict(K=0), INVALID), (dict(H=-8), INVALID), (dict(od=3), INVALID),
+    (dict(dd=2), INVALID), (dict(T=1 << 31, K=2), INVALID),
+    (dict(H=12, dd=1), ALIGNMENT),  # 24-byte rows
+    (dict(H=6, dd=0), ALIGNMENT),
+    (dict(ptrs=(FAKE_MIS, FAKE, FAKE, FAKE)), ALIGNMENT),
+    (dict(ptrs=(FAKE, FAKE, FAKE, None)), INVALID),
+    (dict(T=0, ptrs=(None,) * 4), OK), (dict(H=0, ptrs=(None,) * 4), OK),
+])
+def test_finalize_validation(lib, kw, code):
+    assert finalize(lib, **kw) == code
+
+
+def test_binding_rejects_host_tensors(lib):
+    x = torch.zeros(4, 8)
+    with pytest.raises(ValueError):
+        binding.moe_finalize(x, torch.zeros(8, 8), torch.zeros(8, dtype=torch.int32),
+                             torch.zeros(4, 2))

@@ -1,0 +1,96 @@
+"""GPU parity: moe_finalize vs the CPU oracle (moe_finalize page:
+description, Args). fp32 output within 1e-5 of the term magnitude, bf16
+output within 1 ulp. Marked gpu."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from permutation_group_limited_amd import workloads as wl
+
+from _gpu import (DEV, assert_finalize_close, gpu_finalize, log, oracle_finalize_from,
+                  term_magnitude)
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _inputs(T, K, H, ddt, wdt, seed):
+    g = torch.Generator().manual_seed(seed)
+    down = torch.randn(T * K, H, generator=g).to(ddt)
+    w = (torch.rand(T, K, generator=g) * 2.0).to(wdt)
+    restore = torch.randperm(T * K, generator=g).numpy().astype(np.uint32)
+    return down, w, restore
+
+
+@pytest.mark.parametrize("ddt", ["f32", "bf16"])
+@pytest.mark.parametrize("wdt", ["f32", "bf16"])
+@pytest.mark.parametrize("odt", ["f32", "bf16"])
+@pytest.mark.parametrize("T,K,H", [(1, 1, 8), (5, 2, 136), (33, 8, 520), (17, 3, 1032),
+                                   (9, 9, 264), (4, 16, 64), (40, 6, 7168), (3, 1, 4096)])
+def test_random_shapes(ddt, wdt, odt, T, K, H):
+    if ddt == "f32" and H % 4 or ddt == "bf16" and H % 8:
+        pytest.skip("row not a multiple of 16 bytes")
+    log("finalize case", ddt, wdt, odt, T, K, H)
+    down, w, restore = _inputs(T, K, H, DT[ddt], DT[wdt], seed=T * 100 + K * 10 + H)
+    got = gpu_finalize(down.to(DEV), restore, w, DT[odt])
+    exp = oracle_finalize_from(down, restore, w, DT[odt])
+    assert_finalize_close(got, exp, term_magnitude(down, restore, w))
+
+
+def test_cancellation_is_judged_against_term_magnitude():
+    T, K, H = 8, 2, 64
+    down = torch.randn(T * K, H)
+    down[1::2] = -down[0::2]
+    w = torch.ones(T, K)
+    restore = np.arange(T * K, dtype=np.uint32)
+    got = gpu_finalize(down.to(DEV), restore, w, torch.float32)
+    assert torch.all(got.cpu() == 0)
+
+
+@pytest.mark.parametrize("name", ["tiny", "mixtral", "dsv3", "decode"])
+def test_workload_full_size(name):
+    wk = wl.WORKLOADS[name]
+    log("finalize workload", wk.describe())
+    s, b = wl.make_scores(wk), wl.make_bias(wk)
+    ids, wts = oracle.router(s.numpy(), b.numpy(), wk.K, wk.n_groups, wk.topk_group,
+                             wk.norm_weights, wk.scale)
+    restore = oracle.create_indices(ids, wk.E)["restore_token_order"]
+    down = wl.make_down(wk, device=DEV)
+    w = torch.from_numpy(wts)
+    got = gpu_finalize(down, restore, w, wk.out_dtype)
+    down_h = down.cpu()
+    exp = oracle_finalize_from(down_h, restore, w, wk.out_dtype)
+    mag = term_magnitude(down_h, restore, w) if wk.out_dtype == torch.float32 else None
+    assert_finalize_close(got, exp, mag)
+
+
+def test_skewed_full_size_sampled_tokens():
+    # full-size launch (7 GiB of down); the oracle checks 2048 sampled tokens,
+    # each of which depends only on its own K rows
+    wk = wl.WORKLOADS["skewed"]
+    log("finalize workload", wk.describe(), "(sampled)")
+    s, b = wl.make_scores(wk), wl.make_bias(wk)
+    ids, wts = oracle.router(s.numpy(), b.numpy(), 8, 8, 4, True, 2.5)
+    restore = oracle.create_indices(ids, 256)["restore_token_order"]
+    down = wl.make_down(wk, device=DEV)
+    got = gpu_finalize(down, restore, torch.from_numpy(wts), torch.bfloat16)
+    rng = np.random.default_rng(0)
+    ts = np.sort(np.concatenate([[0, wk.T - 1], rng.choice(wk.T, 2046, replace=False)]))
+    rows = restore.reshape(wk.T, 8)[ts].reshape(-1).astype(np.int64)
+    sub_down = down[torch.from_numpy(rows).to(DEV)].cpu()
+    sub_w = torch.from_numpy(wts[ts])
+    exp = oracle_finalize_from(sub_down, np.arange(rows.size, dtype=np.uint32), sub_w,
+                               torch.bfloat16)
+    assert_finalize_close(got[torch.from_numpy(ts).to(DEV)], exp, None)
+
+
+def test_deterministic():
+    T, K, H = 512, 8, 7168
+    down, w, restore = _inputs(T, K, H, torch.bfloat16, torch.float32, seed=1)
+    dd = down.to(DEV)
+    a = gpu_finalize(dd, restore, w, torch.bfloat16).cpu()
+    for _ in range(3):
+        assert torch.equal(gpu_finalize(dd, restore, w, torch.bfloat16).cpu().view(torch.int16),
+                           a.view(torch.int16))

@@ -1,0 +1,86 @@
+"""GPU parity: moe_create_indices vs the CPU oracle (moe_create_indices
+page: description, Args). Every output bit-exact. Marked gpu."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from permutation_group_limited_amd import workloads as wl
+
+from _gpu import assert_indices_equal, gpu_indices, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["tiny", "mixtral", "dsv3", "decode", "skewed"])
+def test_workload_router_output(name):
+    w = wl.WORKLOADS[name]
+    log("indices workload", w.describe())
+    s, b = wl.make_scores(w), wl.make_bias(w)
+    ids, _ = oracle.router(s.numpy(), b.numpy(), w.K, w.n_groups, w.topk_group,
+                           w.norm_weights, w.scale)
+    got = gpu_indices(ids, w.E)
+    exp = oracle.create_indices(ids, w.E)
+    assert_indices_equal(got, exp)
+    if name == "skewed":
+        assert exp["expert_usage_stats"][0] > 8192  # the skew this workload is for
+
+
+SIZES = [0, 1, 2, 63, 64, 65, 255, 256, 257, 1000, 4095, 4096, 4097, 4352, 8192, 65536,
+         65537, 100000, 524288, 1 << 20]
+
+
+@pytest.mark.parametrize("N", SIZES)
+@pytest.mark.parametrize("E", [1, 3, 8, 256, 1000, 1024])
+def test_random_ids(N, E):
+    if N > 100000 and E not in (8, 256):
+        pytest.skip("large N covered for E = 8 and 256")
+    log("indices case N", N, "E", E)
+    ids = wl.random_ids(N, E, seed=N * 31 + E).numpy()
+    assert_indices_equal(gpu_indices(ids, E), oracle.create_indices(ids, E))
+
+
+@pytest.mark.parametrize("N", [5000, 524288])
+def test_skewed_ids(N):
+    ids = wl.random_ids(N, 256, seed=N, skew=1.5).numpy()
+    assert_indices_equal(gpu_indices(ids, 256), oracle.create_indices(ids, 256))
+
+
+def test_single_expert_everywhere():
+    ids = np.full(70000, 17, np.int32)
+    assert_indices_equal(gpu_indices(ids, 256), oracle.create_indices(ids, 256))
+
+
+def test_sorted_and_reversed_ids():
+    ids = np.sort(wl.random_ids(30000, 256, seed=3).numpy())
+    assert_indices_equal(gpu_indices(ids, 256), oracle.create_indices(ids, 256))
+    ids = ids[::-1].copy()
+    assert_indices_equal(gpu_indices(ids, 256), oracle.create_indices(ids, 256))
+
+
+def test_deterministic_skewed():
+    w = wl.WORKLOADS["skewed"]
+    s, b = wl.make_scores(w), wl.make_bias(w)
+    ids, _ = oracle.router(s.numpy(), b.numpy(), 8, 8, 4, True, 2.5)
+    first = gpu_indices(ids, 256)
+    for _ in range(5):
+        assert_indices_equal(gpu_indices(ids, 256), first)
+
+
+def test_out_of_range_ids_stay_contained():
+    # precondition violated on purpose: the kernels skip such slots (they
+    # never form an address from them) and mark their restore entry
+    ids = wl.random_ids(3000, 64, seed=9).numpy()
+    bad = np.array([5, 77, 1500, 2999])
+    ids[bad] = [64, -1, 1000, 2 ** 31 - 1]
+    got = gpu_indices(ids, 64)
+    assert np.all(got["restore_token_order"][bad] == 0xFFFFFFFF)
+    keep = np.setdiff1d(np.arange(ids.size), bad)
+    ref = oracle.create_indices(ids[keep], 64)
+    n = keep.size
+    assert np.array_equal(got["expert_ids"], ref["expert_ids"])
+    assert np.array_equal(got["expert_usage_stats"], ref["expert_usage_stats"])
+    assert np.array_equal(got["expert_start_indices"], ref["expert_start_indices"])
+    # the valid slots keep their own (uncompacted) indices
+    assert np.array_equal(got["token_expert_order"][:n], keep[ref["token_expert_order"]])
+    assert np.array_equal(got["restore_token_order"][keep], ref["restore_token_order"])

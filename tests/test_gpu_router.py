@@ -1,0 +1,88 @@
+"""GPU parity: moe_router_group_limited vs the CPU oracle (router page:
+description, Parameters, Args). Indices bit-exact, weights within 1e-6
+relative. Marked gpu: needs an MI355X."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from permutation_group_limited_amd import workloads as wl
+
+from _gpu import assert_weights_close, gpu_router, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["tiny", "mixtral", "dsv3", "decode", "skewed"])
+def test_workload_full_size(name):
+    w = wl.WORKLOADS[name]
+    log("router workload", w.describe())
+    s, b = wl.make_scores(w), wl.make_bias(w)
+    for mode in (oracle.GROUP_TOP2_SUM, oracle.GROUP_MAX):
+        gi, gw = gpu_router(s, b, w.K, w.n_groups, w.topk_group, w.norm_weights, w.scale, mode)
+        oi, ow = oracle.router(s.numpy(), b.numpy(), w.K, w.n_groups, w.topk_group,
+                               w.norm_weights, w.scale, mode)
+        assert np.array_equal(gi, oi), "indices differ in %d tokens" % np.sum(np.any(gi != oi, 1))
+        assert_weights_close(gw, ow)
+
+
+CASES = [
+    # (T, E, G, TG, K)
+    (1, 1, 1, 1, 1), (5, 2, 1, 1, 2), (7, 4, 2, 1, 2), (33, 8, 1, 1, 2), (33, 8, 4, 2, 3),
+    (65, 8, 8, 3, 3), (100, 16, 4, 2, 4), (129, 32, 8, 4, 6), (257, 64, 8, 4, 8),
+    (1000, 64, 64, 7, 5), (300, 128, 8, 4, 8), (300, 128, 4, 1, 16), (511, 256, 8, 4, 8),
+    (77, 256, 1, 1, 8), (77, 256, 16, 5, 10), (77, 256, 64, 32, 64), (77, 256, 256 // 4, 2, 8),
+    (130, 512, 8, 4, 8), (130, 512, 32, 3, 12), (61, 1024, 8, 4, 8), (61, 1024, 64, 64, 64),
+]
+
+
+@pytest.mark.parametrize("T,E,G,TG,K", CASES)
+@pytest.mark.parametrize("levels", [0, 3])
+def test_random_shapes(T, E, G, TG, K, levels):
+    log("router case", T, E, G, TG, K, "levels", levels)
+    s = wl.random_scores(T, E, seed=T + E + K, levels=levels)
+    b = wl.random_bias(E, seed=G + TG, std=0.02, levels=levels)
+    for mode in (oracle.GROUP_TOP2_SUM, oracle.GROUP_MAX):
+        for norm in (True, False):
+            gi, gw = gpu_router(s, b, K, G, TG, norm, 1.75, mode)
+            oi, ow = oracle.router(s.numpy(), b.numpy(), K, G, TG, norm, 1.75, mode)
+            assert np.array_equal(gi, oi), (mode, norm)
+            assert_weights_close(gw, ow)
+
+
+def test_all_ties():
+    # every score equal: selection is decided by the index rule alone
+    T, E = 50, 256
+    s = torch.full((T, E), 0.5)
+    b = torch.zeros(E)
+    gi, _ = gpu_router(s, b, 8, 8, 4, True, 1.0)
+    oi, _ = oracle.router(s.numpy(), b.numpy(), 8, 8, 4, True, 1.0)
+    assert np.array_equal(gi, oi)
+    assert gi[0].tolist() == list(range(8))
+
+
+def test_signed_zero_scores_tie():
+    # -0 and +0 compare equal: lower index wins
+    T, E = 4, 8
+    s = torch.zeros(T, E)
+    s[:, ::2] = -0.0
+    b = torch.zeros(E)
+    gi, _ = gpu_router(s, b, 3, 1, 1, False, 1.0)
+    oi, _ = oracle.router(s.numpy(), b.numpy(), 3, 1, 1, False, 1.0)
+    assert np.array_equal(gi, oi)
+    assert gi[0].tolist() == [0, 1, 2]
+
+
+def test_empty_batch():
+    gi, gw = gpu_router(torch.zeros(0, 256), torch.zeros(256), 8, 8, 4, True, 1.0)
+    assert gi.shape == (0, 8) and gw.shape == (0, 8)
+
+
+def test_deterministic():
+    w = wl.WORKLOADS["dsv3"]
+    s, b = wl.make_scores(w), wl.make_bias(w)
+    a = gpu_router(s, b, 8, 8, 4, True, 2.5)
+    for _ in range(3):
+        c = gpu_router(s, b, 8, 8, 4, True, 2.5)
+        assert np.array_equal(a[0], c[0]) and np.array_equal(a[1].view(np.uint32),
+                                                             c[1].view(np.uint32))
