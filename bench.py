@@ -112,35 +112,48 @@ def main():
     out = torch.empty(T, H, dtype=wk.out_dtype, device=dev)
 
     def step(ev=None):
-        binding.moe_router_group_limited(idx, wts, scores, bias, wk.n_groups, wk.topk_group,
-                                         wk.norm_weights, wk.scale)
-        binding.moe_create_indices(order, starts, restore, eids, stats, idx, ws)
         if ev is not None:
             ev[0].record()
-        binding.moe_finalize(out, down, restore, wts)
+        binding.moe_router_group_limited(idx, wts, scores, bias, wk.n_groups, wk.topk_group,
+                                         wk.norm_weights, wk.scale)
         if ev is not None:
             ev[1].record()
+        binding.moe_create_indices(order, starts, restore, eids, stats, idx, ws)
+        if ev is not None:
+            ev[2].record()
+        binding.moe_finalize(out, down, restore, wts)
+        if ev is not None:
+            ev[3].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    fin_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    # timed region 1 (headline): K back-to-back steps between two events
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     t_start.record()
-    for i in range(args.steps):
-        step(fin_ev[i])
+    for _ in range(args.steps):
+        step()
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     elapsed_ms = t_start.elapsed_time(t_end)
-    fin_ms = [a.elapsed_time(b) for a, b in fin_ev]
     ms_per_step = elapsed_ms / args.steps
-    fin_avg_ms = sum(fin_ms) / len(fin_ms)
+
+    # timed region 2: the same K steps with events between the stages, on
+    # the launch stream, for per-stage durations (events add small gaps, so
+    # the headline comes from region 1)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    stage_ms = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
+                for j, name in enumerate(("router", "create_indices", "finalize"))}
+    fin_avg_ms = stage_ms["finalize"]
 
     bytes_router = T * E * 4 + E * 4 + N * (4 + 4)
     bytes_indices = N * 4 + 2 * N * 4 + (2 * E + 1) * 4 + 8
@@ -171,7 +184,7 @@ def main():
         "algorithmic_bytes_per_step": bytes_total,
         "stage_bytes": {"router": bytes_router, "create_indices": bytes_indices,
                         "finalize": bytes_finalize},
-        "finalize_ms": fin_avg_ms,
+        "stage_ms": stage_ms,
         "wall_s": wall,
         "roofline": {"kernel": "finalize_kernel", "bound": "hbm", "achieved": fin_gbps,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": fin_gbps / PEAK_HBM_GBPS,

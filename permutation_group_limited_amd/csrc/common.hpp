@@ -34,9 +34,9 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 // Monotone map binary32 -> uint32 for finite inputs: a < b  <=>  key(a) <
 // key(b), and -0 / +0 map to the same key (IEEE equality).
 __device__ __forceinline__ uint32_t ordered_key(float v) {
-  uint32_t u = __float_as_uint(v);
-  if (v == 0.0f) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = (v == 0.0f) ? 0u : __float_as_uint(v);
+  const uint32_t flip = static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u;
+  return u ^ flip;  // negative: all bits flipped; positive: sign bit set
 }
 
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
@@ -74,6 +74,7 @@ moe_status_t launch_router(int32_t* expert_indices, float* expert_weights, const
                            hipStream_t stream);
 
 struct IndexPlan {
+  int waves;        // waves per workgroup (16 when E <= 256, else 4)
   int64_t chunk;    // slots per workgroup
   int64_t nchunks;  // workgroups of the scatter (and histogram) launch
   int rounds;       // 64-slot rounds per wave

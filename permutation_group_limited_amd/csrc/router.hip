@@ -8,12 +8,20 @@
 // Mapping (CDNA-specific; the page's one-thread-per-expert block is not
 // used): a token is owned by LPT consecutive lanes of a wave64, each lane
 // holding EPL consecutive experts (E = LPT * EPL). For E >= 64 a token fills
-// a whole wave (E = 256: 4 experts = one 16-byte load per lane); for E < 64
-// several tokens share a wave. A group of S = E / n_groups experts is then
-// LPG = S / EPL adjacent lanes, so group top-2 is a log2(LPG)-step xor
-// butterfly; the top-K is K rounds of a lexicographic argmax over the token's
-// lanes on 64-bit keys (ordered score, inverted expert id), which breaks
-// ties towards the lower expert id by construction.
+// a whole wave (E = 256: 4 experts, one 16-byte load per lane); for E < 64
+// several tokens share a wave.
+//
+//  * group score: lane-local top-2, then a top-2 merge over the LPG = S/EPL
+//    lanes of a group through DPP (quad_perm, row_half_mirror, row_mirror),
+//    ds_swizzle and, for 64-lane groups, ds_bpermute; groups are ranked by
+//    counting the groups that beat each one (ties: lower group index).
+//  * top-K: each lane sorts its EPL (key, expert) pairs (key = biased score
+//    mapped to an order-preserving uint32); then K rounds of: segment max of
+//    the lane heads (DPP max steps and v_readlane), a ballot of the lanes
+//    whose head equals it, the lowest such lane wins (lowest expert id: the
+//    lower-index tie rule) and pops its head. Round k fills slot k, so the
+//    slots come out in (score desc, id asc) order.
+//  * weights: the K winners' unbiased scores, summed in slot order.
 #include "common.hpp"
 
 namespace moe {
@@ -40,6 +48,92 @@ __device__ __forceinline__ void load_row(float (&dst)[EPL], const float* __restr
   }
 }
 
+// Cross-lane moves inside rows of 16 lanes. Every control used here reads a
+// lane of the same row, so no lane is left without a source; the moves are
+// written so that the compiler can fold them into the consuming VALU op.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), CTRL, 0xF, 0xF, true));
+}
+constexpr int kXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141;  // lane i <-> 7-i within each 8 lanes
+constexpr int kMirror = 0x140;      // lane i <-> 15-i within each row
+
+// Merge the (largest, second largest) pair of this lane with the pair of
+// the lane that holds a disjoint set of experts.
+__device__ __forceinline__ void merge_top2(float& m1, float& m2, float o1, float o2) {
+  const float n2 = fmaxf(fminf(m1, o1), fmaxf(m2, o2));
+  m1 = fmaxf(m1, o1);
+  m2 = n2;
+}
+
+// Top-2 over groups of `lpg` adjacent lanes (lpg a power of two, groups
+// aligned). Each step pairs lanes whose partial results cover disjoint
+// experts: xor 1 and xor 2 (quad_perm), then the mirrored half-row and row
+// (every lane of a quad, resp. half-row, already holds the same pair), then
+// xor 16 (ds_swizzle) and xor 32 (ds_bpermute).
+__device__ __forceinline__ void group_top2(float& m1, float& m2, int lpg) {
+  if (lpg >= 2) merge_top2(m1, m2, dpp_f<kXor1>(m1), dpp_f<kXor1>(m2));
+  if (lpg >= 4) merge_top2(m1, m2, dpp_f<kXor2>(m1), dpp_f<kXor2>(m2));
+  if (lpg >= 8) merge_top2(m1, m2, dpp_f<kHalfMirror>(m1), dpp_f<kHalfMirror>(m2));
+  if (lpg >= 16) merge_top2(m1, m2, dpp_f<kMirror>(m1), dpp_f<kMirror>(m2));
+  if (lpg >= 32) {
+    const float o1 = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(m1), 0x401F));
+    const float o2 = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(m2), 0x401F));
+    merge_top2(m1, m2, o1, o2);
+  }
+  if (lpg >= 64) merge_top2(m1, m2, __shfl_xor(m1, 32, kWave), __shfl_xor(m2, 32, kWave));
+}
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// Maximum of v over the token's LPT lanes, returned to every lane of the
+// segment: xor 1 and xor 2 inside quads, mirrored half-rows and rows (by
+// then each quad, resp. half-row, is uniform), xor 16 by ds_swizzle; for a
+// full wave the four row maxima are combined through v_readlane.
+template <int LPT>
+__device__ __forceinline__ uint32_t segment_max(uint32_t v) {
+  if (LPT >= 2) v = umax(v, dpp_u<kXor1>(v));
+  if (LPT >= 4) v = umax(v, dpp_u<kXor2>(v));
+  if (LPT >= 8) v = umax(v, dpp_u<kHalfMirror>(v));
+  if (LPT >= 16) v = umax(v, dpp_u<kMirror>(v));
+  if constexpr (LPT == 32) {
+    v = umax(v, static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), 0x401F)));
+  } else if constexpr (LPT == kWave) {
+    const int x = static_cast<int>(v);
+    v = umax(umax(static_cast<uint32_t>(__builtin_amdgcn_readlane(x, 0)),
+                  static_cast<uint32_t>(__builtin_amdgcn_readlane(x, 16))),
+             umax(static_cast<uint32_t>(__builtin_amdgcn_readlane(x, 32)),
+                  static_cast<uint32_t>(__builtin_amdgcn_readlane(x, 48))));
+  }
+  return v;
+}
+
+// Stable descending sort of keys held in registers, carrying each key's
+// element index along: adjacent exchanges that swap only on a strictly
+// larger key keep equal keys in ascending element order.
+template <int EPL>
+__device__ __forceinline__ void sort_desc(uint32_t (&k)[EPL], uint32_t (&e)[EPL]) {
+#pragma unroll
+  for (int i = 1; i < EPL; ++i) {
+#pragma unroll
+    for (int j = i; j > 0; --j) {
+      const bool sw = k[j] > k[j - 1];
+      const uint32_t k0 = sw ? k[j] : k[j - 1], k1 = sw ? k[j - 1] : k[j];
+      const uint32_t e0 = sw ? e[j] : e[j - 1], e1 = sw ? e[j - 1] : e[j];
+      k[j - 1] = k0;
+      k[j] = k1;
+      e[j - 1] = e0;
+      e[j] = e1;
+    }
+  }
+}
+
 template <int EPL, int LPT>
 __global__ __launch_bounds__(kBlock) void router_kernel(
     int32_t* __restrict__ out_idx, float* __restrict__ out_w, const float* __restrict__ scores,
@@ -55,6 +149,8 @@ __global__ __launch_bounds__(kBlock) void router_kernel(
       (static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave) * TPW + lane / LPT;
   const bool tok_ok = t < T;
   const int e0 = sub * EPL;
+  const uint64_t segmask =
+      (LPT == kWave) ? ~0ull : (((1ull << LPT) - 1ull) << tok_lane0);
 
   float s[EPL], bi[EPL], b[EPL];
   if (tok_ok) {
@@ -65,97 +161,99 @@ __global__ __launch_bounds__(kBlock) void router_kernel(
   }
   load_row<EPL>(bi, bias + e0);
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    b[i] = s[i] + bi[i];
-    if (b[i] == 0.0f) b[i] = 0.0f;  // one zero: -0 and +0 tie anyway
-  }
+  for (int i = 0; i < EPL; ++i) b[i] = s[i] + bi[i];
 
   // ---- group stage: keep the best topk_group groups ------------------------
   bool kept = true;
   if (topk_group < n_groups) {
-    const int S = E / n_groups;
+    // E, n_groups and EPL are powers of two: shifts, not divisions
+    const int lg_groups = __builtin_ctz(static_cast<uint32_t>(n_groups));
+    const int S = E >> lg_groups;
     const int LPG = S / EPL;  // lanes per group, a power of two
+    const int lg_lpg = __builtin_ctz(static_cast<uint32_t>(LPG));
     float m1 = -__builtin_inff(), m2 = -__builtin_inff();
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-      if (b[i] > m1) {
-        m2 = m1;
-        m1 = b[i];
-      } else if (b[i] > m2) {
-        m2 = b[i];
-      }
+      m2 = fmaxf(m2, fminf(m1, b[i]));
+      m1 = fmaxf(m1, b[i]);
     }
-    for (int off = 1; off < LPG; off <<= 1) {
-      const float o1 = __shfl_xor(m1, off, kWave);
-      const float o2 = __shfl_xor(m2, off, kWave);
-      const float n2 = fmaxf(fminf(m1, o1), fmaxf(m2, o2));
-      m1 = fmaxf(m1, o1);
-      m2 = n2;
-    }
+    group_top2(m1, m2, LPG);
     const float gs = (mode == MOE_GROUP_MAX || S == 1) ? m1 : m1 + m2;
-    const int my_g = sub / LPG;
+    const int my_g = sub >> lg_lpg;
     int rank = 0;
-    for (int g = 0; g < n_groups; ++g) {
-      const float o = __shfl(gs, tok_lane0 + g * LPG, kWave);
-      rank += (o > gs) || (o == gs && g < my_g);
+    if constexpr (LPT == kWave) {
+      for (int g = 0; g < n_groups; ++g) {
+        const float o = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gs), g * LPG));
+        rank += (o > gs) || (o == gs && g < my_g);
+      }
+    } else {
+      for (int g = 0; g < n_groups; ++g) {
+        const float o = __shfl(gs, tok_lane0 + g * LPG, kWave);
+        rank += (o > gs) || (o == gs && g < my_g);
+      }
     }
     kept = rank < topk_group;
   }
 
-  // ---- top-K over the surviving experts -----------------------------------
-  // key = ordered(b) << 32 | ~e; 0 marks "not a candidate" (every finite
-  // score has ordered key >= 0x00800000).
-  uint64_t keys[EPL];
+  // ---- top-K: K rounds of segment max over the lanes' sorted heads ---------
+  // Keys preserve the order of the biased scores (0 = not a candidate). Each
+  // lane sorts its EPL (key, element) pairs by key desc, element asc. A
+  // round takes the segment maximum of the lane heads; among lanes whose
+  // head equals it the lowest lane wins, which is the lowest expert id
+  // because lanes hold ascending, disjoint id ranges. The winner pops its
+  // head. Round k yields slot k.
+  uint32_t kv[EPL];
+  uint32_t ki[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
-    keys[i] = (tok_ok && kept)
-                  ? (static_cast<uint64_t>(ordered_key(b[i])) << 32) |
-                        static_cast<uint32_t>(~static_cast<uint32_t>(e0 + i))
-                  : 0ull;
+    kv[i] = (tok_ok && kept) ? ordered_key(b[i]) : 0u;
+    ki[i] = static_cast<uint32_t>(i);
   }
-  // lane-local descending sort (EPL <= 16, insertion network, unrolled)
-#pragma unroll
-  for (int i = 1; i < EPL; ++i) {
-#pragma unroll
-    for (int j = i; j > 0; --j) {
-      const uint64_t hi = keys[j - 1] > keys[j] ? keys[j - 1] : keys[j];
-      const uint64_t lo = keys[j - 1] > keys[j] ? keys[j] : keys[j - 1];
-      keys[j - 1] = hi;
-      keys[j] = lo;
-    }
-  }
+  sort_desc<EPL>(kv, ki);
 
-  uint64_t mine = 0;
+  uint32_t my_id = 0;
   for (int k = 0; k < K; ++k) {
-    uint64_t best = keys[0];
-#pragma unroll
-    for (int off = 1; off < LPT; off <<= 1) {
-      const uint64_t o = shfl_xor_u64(best, off);
-      best = o > best ? o : best;
+    const uint32_t head = kv[0];
+    const uint64_t bal = __ballot(head == segment_max<LPT>(head)) & segmask;
+    const int win = __builtin_ctzll(static_cast<unsigned long long>(bal));
+    uint32_t id;
+    if constexpr (LPT == kWave) {
+      id = static_cast<uint32_t>(win * EPL) +
+           static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ki[0]), win));
+    } else {
+      id = static_cast<uint32_t>(win - tok_lane0);  // one expert per lane
     }
-    if (sub == k) mine = best;
-    if (keys[0] == best) {  // the owner pops its head
+    if (sub == k) my_id = id;
+    if (lane == win) {
 #pragma unroll
-      for (int i = 0; i + 1 < EPL; ++i) keys[i] = keys[i + 1];
-      keys[EPL - 1] = 0ull;
+      for (int i = 0; i + 1 < EPL; ++i) {
+        kv[i] = kv[i + 1];
+        ki[i] = ki[i + 1];
+      }
+      kv[EPL - 1] = 0u;
     }
   }
 
   // ---- weights from the unbiased scores -----------------------------------
   const bool slot = tok_ok && sub < K;
-  uint32_t e_sel = ~static_cast<uint32_t>(mine);
-  if (e_sel >= static_cast<uint32_t>(E)) e_sel = 0;  // only reachable with NaN scores
-  const float u = slot ? scores[t * E + e_sel] : 0.0f;
+  if (my_id >= static_cast<uint32_t>(E)) my_id = 0;  // unreachable with finite scores
+  const float u = slot ? scores[t * E + my_id] : 0.0f;
   float w;
   if (norm_weights) {
     float d = 0.0f;
-    for (int k = 0; k < K; ++k) d += __shfl(u, tok_lane0 + k, kWave);
+    if constexpr (LPT == kWave) {
+      for (int q = 0; q < K; ++q)
+        d += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, u), q));
+    } else {
+      for (int q = 0; q < K; ++q) d += __shfl(u, tok_lane0 + q, kWave);
+    }
     w = (u / d) * scale;
   } else {
     w = u * scale;
   }
   if (slot) {
-    out_idx[t * K + sub] = static_cast<int32_t>(e_sel);
+    out_idx[t * K + sub] = static_cast<int32_t>(my_id);
     out_w[t * K + sub] = w;
   }
 }
