@@ -12,12 +12,13 @@ groups (4 kept), K=8, hidden 7168, bf16 expert outputs and output. One
 routed token-slot is one (token, k) pair, i.e. one row of `down`.
 
 Reported beside the throughput:
+  * per-stage mean durations: each stage K times back to back on the launch
+    stream between two HIP events;
   * roofline of the dominant kernel (finalize): algorithmic bytes per launch
     (T*K*H*2 read + T*K*(4+4) restore and weights + T*H*2 written) divided by
-    its mean duration from HIP events recorded around each finalize launch
-    on the launch stream inside the timed region, against 8 TB/s; plus the
-    HBM bytes measured by rocprofv3 counters when the committed counter
-    summary matches the current kernel source;
+    its mean duration above, against 8 TB/s; plus the HBM bytes measured by
+    rocprofv3 counters when the committed counter summary matches the
+    current kernel source;
   * cpu_baseline: the CPU oracle (plain C, OpenMP over tokens) timed on the
     host cores over whole steps of the same workload, and a parity check of
     the GPU step against it.
@@ -50,6 +51,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time for the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="after the run, copy BYTES with torch's plain copy kernel (3 times): "
+                         "the reference dispatch for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE")
     return ap.parse_args()
 
 
@@ -111,19 +115,20 @@ def main():
                      dtype=torch.int32, device=dev)
     out = torch.empty(T, H, dtype=wk.out_dtype, device=dev)
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
+    def router():
         binding.moe_router_group_limited(idx, wts, scores, bias, wk.n_groups, wk.topk_group,
                                          wk.norm_weights, wk.scale)
-        if ev is not None:
-            ev[1].record()
+
+    def indices():
         binding.moe_create_indices(order, starts, restore, eids, stats, idx, ws)
-        if ev is not None:
-            ev[2].record()
+
+    def finalize():
         binding.moe_finalize(out, down, restore, wts)
-        if ev is not None:
-            ev[3].record()
+
+    def step():
+        router()
+        indices()
+        finalize()
 
     for _ in range(args.warmup):
         step()
@@ -143,15 +148,23 @@ def main():
     elapsed_ms = t_start.elapsed_time(t_end)
     ms_per_step = elapsed_ms / args.steps
 
-    # timed region 2: the same K steps with events between the stages, on
-    # the launch stream, for per-stage durations (events add small gaps, so
-    # the headline comes from region 1)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # timed region 2: each stage K times back to back on the launch stream
+    # (every stage is idempotent on its inputs), bracketed by events, for
+    # per-stage mean durations; finalize's is the roofline's denominator
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(evs[i])
+    ev[0].record()
+    for _ in range(args.steps):
+        router()
+    ev[1].record()
+    for _ in range(args.steps):
+        indices()
+    ev[2].record()
+    for _ in range(args.steps):
+        finalize()
+    ev[3].record()
     torch.cuda.synchronize()
-    stage_ms = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
+    stage_ms = {name: ev[j].elapsed_time(ev[j + 1]) / args.steps
                 for j, name in enumerate(("router", "create_indices", "finalize"))}
     fin_avg_ms = stage_ms["finalize"]
 
@@ -190,6 +203,15 @@ def main():
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": fin_gbps / PEAK_HBM_GBPS,
                      "traffic": traffic},
     }
+
+    if args.copy_probe > 0:
+        src = torch.ones(args.copy_probe // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_probe_bytes"] = args.copy_probe
+        del src, dst
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity"] = cpu_leg(

@@ -9,8 +9,9 @@
 // column chunk of the row). The wave's token is uniform, so its K restore
 // entries and K weights come in through scalar loads; each lane then issues
 // K independent 16-byte non-temporal loads (one per gathered row, all in
-// flight together), folds them with one fmaf per element in ascending k, and
-// writes its output slice with one store. Rows are addressed in 64 bits
+// flight together; every row segment is read exactly once), folds them with
+// one fmaf per element in ascending k, and writes its output slice with one
+// ordinary store (measured a little faster than a non-temporal store here). Rows are addressed in 64 bits
 // (T*K*H elements exceed 2^32 for large prefill batches).
 #include "common.hpp"
 
@@ -57,14 +58,14 @@ __device__ __forceinline__ void store_out<uint16_t, 8>(uint16_t* p, const float*
   v.y = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
   v.z = f32_to_bf16_bits(acc[4]) | (f32_to_bf16_bits(acc[5]) << 16);
   v.w = f32_to_bf16_bits(acc[6]) | (f32_to_bf16_bits(acc[7]) << 16);
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+  *reinterpret_cast<u32x4*>(p) = v;
 }
 template <>
 __device__ __forceinline__ void store_out<uint16_t, 4>(uint16_t* p, const float* acc) {
   u32x2 v;
   v.x = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);
   v.y = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+  *reinterpret_cast<u32x2*>(p) = v;
 }
 template <>
 __device__ __forceinline__ void store_out<float, 4>(float* p, const float* acc) {
@@ -73,7 +74,7 @@ __device__ __forceinline__ void store_out<float, 4>(float* p, const float* acc) 
   v.y = __float_as_uint(acc[1]);
   v.z = __float_as_uint(acc[2]);
   v.w = __float_as_uint(acc[3]);
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+  *reinterpret_cast<u32x4*>(p) = v;
 }
 template <>
 __device__ __forceinline__ void store_out<float, 8>(float* p, const float* acc) {

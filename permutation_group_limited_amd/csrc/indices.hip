@@ -160,19 +160,38 @@ __global__ __launch_bounds__(W * kWave) void index_scatter_kernel(
   const int64_t w0 = c0 + static_cast<int64_t>(wave) * rounds * kWave;
   uint32_t* my_base = wbase + wave * E;
 
+  // Issue the first batch of ids and this thread's share of the counts
+  // matrix before anything waits on memory, so the two latencies overlap.
+  int32_t first[kBatch];
+  load_batch(first, ids, w0, 0, rounds, c1, lane);
+  const bool split = nchunks > 1 && E <= kThreads;
+  const int parts = E <= kThreads ? kThreads / E : 1;
+  const int my_e = static_cast<int>(threadIdx.x) % E;
+  const int my_part = static_cast<int>(threadIdx.x) / E;
+  constexpr int kCountRegs = 16;
+  uint32_t cv[kCountRegs];
+  const bool cv_resident = split && nchunks <= static_cast<int64_t>(kCountRegs) * parts;
+  if (cv_resident) {
+#pragma unroll
+    for (int q = 0; q < kCountRegs; ++q) {
+      const int64_t c = my_part + static_cast<int64_t>(q) * parts;
+      cv[q] = (my_part < parts && c < nchunks) ? counts[c * E + my_e] : 0u;
+    }
+  }
+
   for (int x = threadIdx.x; x < W * E; x += kThreads) wbase[x] = 0u;
   __syncthreads();
 
   // (a) per-wave histogram. One lane per distinct expert per round writes,
   // and a wave's rounds are in program order, so no atomics are needed. The
   // first batch of ids stays in registers for (e).
-  int32_t first[kBatch];
   for (int r0 = 0; r0 < rounds; r0 += kBatch) {
     int32_t ev[kBatch];
-    load_batch(ev, ids, w0, r0, rounds, c1, lane);
     if (r0 == 0) {
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) first[j] = ev[j];
+      for (int j = 0; j < kBatch; ++j) ev[j] = first[j];
+    } else {
+      load_batch(ev, ids, w0, r0, rounds, c1, lane);
     }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
@@ -194,17 +213,21 @@ __global__ __launch_bounds__(W * kWave) void index_scatter_kernel(
   // (thread part*E + e reads chunks part, part + P, ...), so each thread has
   // at most nchunks / P loads in flight, and are folded through LDS.
   const int EPT = (E + kThreads - 1) / kThreads;
-  const int parts = E <= kThreads ? kThreads / E : 1;
   uint32_t tot[kMaxEPT], pre[kMaxEPT], start[kMaxEPT];
   uint32_t local_sum = 0, local_active = 0, local_max = 0;
-  if (nchunks > 1 && E <= kThreads) {
-    const int e = static_cast<int>(threadIdx.x) % E;
-    const int part = static_cast<int>(threadIdx.x) / E;
+  if (split) {
     uint32_t a = 0, p = 0;
-    if (part < parts) {
+    if (cv_resident) {
+#pragma unroll
+      for (int q = 0; q < kCountRegs; ++q) {
+        const int64_t c = my_part + static_cast<int64_t>(q) * parts;
+        a += cv[q];
+        p += (c < chunk_id) ? cv[q] : 0u;
+      }
+    } else if (my_part < parts) {
 #pragma unroll 16
-      for (int64_t c = part; c < nchunks; c += parts) {
-        const uint32_t v = counts[c * E + e];
+      for (int64_t c = my_part; c < nchunks; c += parts) {
+        const uint32_t v = counts[c * E + my_e];
         a += v;
         p += (c < chunk_id) ? v : 0u;
       }

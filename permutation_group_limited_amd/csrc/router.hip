@@ -92,6 +92,17 @@ __device__ __forceinline__ void group_top2(float& m1, float& m2, int lpg) {
 
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
+// Sum over groups of `lpg` adjacent lanes, same lane pairing as group_top2.
+__device__ __forceinline__ int group_sum(int x, int lpg) {
+  if (lpg >= 2) x += __builtin_amdgcn_mov_dpp(x, kXor1, 0xF, 0xF, true);
+  if (lpg >= 4) x += __builtin_amdgcn_mov_dpp(x, kXor2, 0xF, 0xF, true);
+  if (lpg >= 8) x += __builtin_amdgcn_mov_dpp(x, kHalfMirror, 0xF, 0xF, true);
+  if (lpg >= 16) x += __builtin_amdgcn_mov_dpp(x, kMirror, 0xF, 0xF, true);
+  if (lpg >= 32) x += __builtin_amdgcn_ds_swizzle(x, 0x401F);
+  if (lpg >= 64) x += __shfl_xor(x, 32, kWave);
+  return x;
+}
+
 // Maximum of v over the token's LPT lanes, returned to every lane of the
 // segment: xor 1 and xor 2 inside quads, mirrored half-rows and rows (by
 // then each quad, resp. half-row, is uniform), xor 16 by ds_swizzle; for a
@@ -179,21 +190,16 @@ __global__ __launch_bounds__(kBlock) void router_kernel(
     }
     group_top2(m1, m2, LPG);
     const float gs = (mode == MOE_GROUP_MAX || S == 1) ? m1 : m1 + m2;
+    // rank of my group = groups that beat it; the LPG lanes of a group split
+    // the comparisons (lane q of the group tests groups q, q + LPG, ...) and
+    // add their counts
     const int my_g = sub >> lg_lpg;
-    int rank = 0;
-    if constexpr (LPT == kWave) {
-      for (int g = 0; g < n_groups; ++g) {
-        const float o = __builtin_bit_cast(
-            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gs), g * LPG));
-        rank += (o > gs) || (o == gs && g < my_g);
-      }
-    } else {
-      for (int g = 0; g < n_groups; ++g) {
-        const float o = __shfl(gs, tok_lane0 + g * LPG, kWave);
-        rank += (o > gs) || (o == gs && g < my_g);
-      }
+    int beats = 0;
+    for (int j = sub & (LPG - 1); j < n_groups; j += LPG) {
+      const float o = __shfl(gs, tok_lane0 + j * LPG, kWave);
+      beats += (o > gs) || (o == gs && j < my_g);
     }
-    kept = rank < topk_group;
+    kept = group_sum(beats, LPG) < topk_group;
   }
 
   // ---- top-K: K rounds of segment max over the lanes' sorted heads ---------
