@@ -35,6 +35,12 @@ _ERRORS = {1: "invalid argument", 2: "input violates a precondition", 3: "out of
 _lib = None
 
 
+def _lib_path() -> str:
+    # MOE_ORACLE_LIB points the wrapper at another build of moe_oracle.c; the
+    # mutation tests use it to check that the pins catch planted mistakes.
+    return os.environ.get("MOE_ORACLE_LIB", _LIB_PATH)
+
+
 def build(force: bool = True) -> str:
     """Compile ``moe_oracle.c`` into ``libmoe_oracle.so`` with gcc."""
     global _lib
@@ -52,9 +58,10 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
+        path = _lib_path()
+        if path == _LIB_PATH and not os.path.exists(_LIB_PATH):
             build()
-        lib = ctypes.CDLL(_LIB_PATH)
+        lib = ctypes.CDLL(path)
         p = ctypes.c_void_p
         i32, i64 = ctypes.c_int32, ctypes.c_int64
         lib.moe_oracle_router.argtypes = [p, p, p, p, i64, i32, i32, i32, i32, i32,

@@ -1,0 +1,95 @@
+"""The oracle's pins must catch plausible mistakes. Each case plants one
+mistake in a copy of oracle/moe_oracle.c (on the CPU: a temporary build that
+nothing else loads), runs the pin tests of that stage against it and expects
+them to fail. A mistake that the pins let through would mean a bug of that
+kind in the oracle could hide."""
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "moe_oracle.c")
+
+ROUTER = "tests/test_oracle_router.py"
+INDICES = "tests/test_oracle_indices.py"
+FINALIZE = "tests/test_oracle_finalize.py"
+
+MUTATIONS = [
+    ("bias left out of the selection", ROUTER,
+     "b[e] = s[e] + bias[e];", "b[e] = s[e];"),
+    ("bias added into the weights", ROUTER,
+     "double w = (double)s[e];", "double w = (double)b[e];"),
+    ("group score is the maximum only", ROUTER,
+     "score = grp[0].v + grp[1].v;", "score = grp[0].v;"),
+    ("group score adds the wrong second term", ROUTER,
+     "score = grp[0].v + grp[1].v;", "score = grp[0].v + grp[S - 1].v;"),
+    ("ties broken towards the higher index", ROUTER,
+     "if (x->id < y->id) return -1;\n    if (x->id > y->id) return 1;",
+     "if (x->id > y->id) return -1;\n    if (x->id < y->id) return 1;"),
+    ("one group too few kept", ROUTER,
+     "for (int32_t r = 0; r < topk_group; ++r)", "for (int32_t r = 0; r + 1 < topk_group; ++r)"),
+    ("group restriction ignored", ROUTER, "if (kept[e / S]) {", "if (1) {"),
+    ("expert-to-group map transposed", ROUTER, "if (kept[e / S]) {", "if (kept[e % n_groups]) {"),
+    ("normalisation skipped", ROUTER, "if (norm_weights) w = w / sum;", ";"),
+    ("scaling factor skipped", ROUTER, "w = w * (double)routed_scaling_factor;", ";"),
+    ("normaliser drops the last weight", ROUTER,
+     "for (int32_t k = 0; k < K; ++k) sum += (double)s[cand[k].id];",
+     "for (int32_t k = 0; k + 1 < K; ++k) sum += (double)s[cand[k].id];"),
+    ("bucket sort not stable", INDICES,
+     "for (int64_t i = 0; i < N; ++i) {\n        const int32_t e = topk_ids[i];",
+     "for (int64_t i = N - 1; i >= 0; --i) {\n        const int32_t e = topk_ids[i];"),
+    ("CSR tail not N", INDICES,
+     "expert_start_indices[j] = (uint32_t)N;", "expert_start_indices[j] = 0;"),
+    ("expert id tail not -1", INDICES, "expert_ids[j] = -1;", "expert_ids[j] = 0;"),
+    ("usage stats swapped", INDICES,
+     "expert_usage_stats[0] = largest;\n    expert_usage_stats[1] = active;",
+     "expert_usage_stats[1] = largest;\n    expert_usage_stats[0] = active;"),
+    ("restore off by one", INDICES,
+     "restore_token_order[i] = p;", "restore_token_order[i] = p + 1 < (uint32_t)N ? p + 1 : p;"),
+    ("order holds the token, not the slot", INDICES,
+     "token_expert_order[p] = (uint32_t)i;", "token_expert_order[p] = (uint32_t)(i / 2);"),
+    ("inactive experts listed", INDICES,
+     "if (count[e] > 0) {\n            expert_ids[active] = e;",
+     "if (count[e] >= 0) {\n            expert_ids[active] = e;"),
+    ("accumulator wider than fp32", FINALIZE,
+     ["float* acc = (float*)malloc(sizeof(float)",
+      "acc[h] = fmaf(w, load_as_f32(down, down_dtype, row * H + h), acc[h]);"],
+     ["double* acc = (double*)malloc(sizeof(double)",
+      "acc[h] = fma((double)w, (double)load_as_f32(down, down_dtype, row * H + h), acc[h]);"]),
+    ("multiply then add instead of a fused multiply-add", FINALIZE,
+     "acc[h] = fmaf(w, load_as_f32(down, down_dtype, row * H + h), acc[h]);",
+     "{ float p_ = w * load_as_f32(down, down_dtype, row * H + h); acc[h] = acc[h] + p_; }"),
+    ("k summed in reverse", FINALIZE,
+     "for (int32_t k = 0; k < K; ++k) {\n                    const int64_t row",
+     "for (int32_t k = K - 1; k >= 0; --k) {\n                    const int64_t row"),
+    ("weight index transposed", FINALIZE,
+     "load_as_f32(router_weight, weight_dtype, t * K + k)",
+     "load_as_f32(router_weight, weight_dtype, (k * T + t) % (T * K))"),
+    ("restore read as its inverse", FINALIZE,
+     "const int64_t row = (int64_t)restore_order[t * K + k];",
+     "int64_t row = 0;\n                    for (int64_t q = 0; q < N; ++q) if (restore_order[q] == (uint32_t)(t * K + k)) row = q;"),
+    ("bf16 conversion truncates", FINALIZE, "u += 0x7fffu + lsb;", "(void)lsb;"),
+    ("bf16 ties rounded away from zero", FINALIZE, "u += 0x7fffu + lsb;", "u += 0x8000u; (void)lsb;"),
+]
+
+
+@pytest.mark.parametrize("name,tests,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_planted_mistake(name, tests, old, new, tmp_path):
+    src = open(SRC).read()
+    olds, news = (old, new) if isinstance(old, list) else ([old], [new])
+    for o, n in zip(olds, news):
+        assert src.count(o) >= 1, "mutation no longer applies: " + name
+        src = src.replace(o, n)
+    mutated = tmp_path / "moe_oracle_mutant.c"
+    mutated.write_text(src)
+    lib = tmp_path / "libmoe_oracle_mutant.so"
+    subprocess.run(["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+                    "-o", str(lib), str(mutated), "-lm"], check=True, capture_output=True)
+    env = dict(os.environ, MOE_ORACLE_LIB=str(lib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        "-m", "not gpu", tests], cwd=ROOT, env=env, capture_output=True, text=True,
+                       timeout=600)
+    assert r.returncode != 0, "pins did not catch: %s\n%s" % (name, r.stdout[-2000:])
