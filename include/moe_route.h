@@ -52,8 +52,11 @@ typedef enum {
 
 typedef enum {
     MOE_DTYPE_F32 = 0,  /* IEEE binary32 */
-    MOE_DTYPE_BF16 = 1  /* bfloat16 (high half of binary32) */
+    MOE_DTYPE_BF16 = 1, /* bfloat16 (high half of binary32) */
+    MOE_DTYPE_F16 = 2   /* IEEE binary16 */
 } moe_dtype_t;
+/* Every value is widened exactly to binary32 on load; every result is
+ * computed in binary32 and rounded to nearest even on store. */
 
 /* How a group of experts is scored before the top-topk_group groups are
  * kept. The router page says only that the groups "with the highest scores"
@@ -69,8 +72,9 @@ typedef enum {
  * nn/moe): description, Parameters and Args.
  *
  *   expert_indices   out int32 [T, K]: selected experts of each token.
- *   expert_weights   out, dtype = scores_dtype, [T, K]: routing weights
- *                    computed from the UNBIASED scores.
+ *   expert_weights   out, dtype = scores_dtype (the page gives the weights
+ *                    the scores' type), [T, K]: routing weights computed
+ *                    from the UNBIASED scores.
  *   expert_scores    in  [T, E] routing scores, dtype scores_dtype.
  *   expert_bias      in  [E] per-expert bias, dtype bias_dtype, added to the
  *                    scores for selection only.
@@ -90,8 +94,9 @@ typedef enum {
  *
  * Validation: T >= 0; E >= 1 and E % n_groups == 0; 1 <= topk_group <=
  * n_groups <= 64; 1 <= K <= topk_group * S; K <= 64; non-NULL pointers when
- * T > 0. Supported: scores/bias F32; E a power of two, 1 <= E <= 1024
- * (other E give MOE_ERR_UNSUPPORTED).
+ * T > 0; expert_scores and expert_bias 16-byte aligned. Supported: scores
+ * F32, BF16 or F16 with bias of the same dtype or F32; E a power of two,
+ * 1 <= E <= 1024 (other E give MOE_ERR_UNSUPPORTED).
  */
 moe_status_t moe_router_group_limited(int32_t* expert_indices, void* expert_weights,
                                       const void* expert_scores, const void* expert_bias,
@@ -161,10 +166,10 @@ moe_status_t moe_create_indices(uint32_t* token_expert_order, uint32_t* expert_s
  *
  * output[t, h] = convert(sum_k w[t,k] * down[restore[t*K+k], h]) with the
  * sum formed in fp32 from +0 by one fused multiply-add per k in ascending k;
- * conversion to bf16 rounds to nearest even.
+ * conversion to bf16 / fp16 rounds to nearest even.
  *
- * Validation: T >= 0, K >= 1, H >= 0, T*K < 2^32; dtypes in {F32, BF16};
- * H * sizeof(down_dtype) and H * sizeof(out_dtype) multiples of 16 bytes;
+ * Validation: T >= 0, K >= 1, H >= 0, T*K < 2^32; dtypes in {F32, BF16,
+ * F16}, any combination; H * sizeof(down_dtype) a multiple of 16 bytes;
  * output and down 16-byte aligned; non-NULL pointers when T*H > 0.
  * Precondition: restore_order[i] < T*K (an out-of-range entry contributes
  * nothing; the output is then unspecified but no access leaves `down`).

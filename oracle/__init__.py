@@ -8,7 +8,8 @@ share no code: the oracle is plain C in ``moe_oracle.c``, compiled with gcc
 arrays.
 
 Conventions of this wrapper:
-  * bf16 arrays are passed and returned as ``numpy.uint16`` bit patterns;
+  * bf16 and fp16 arrays are passed and returned as ``numpy.uint16`` bit
+    patterns, with a dtype code (BF16 or F16) saying which;
   * fp32 arrays as ``numpy.float32``; index arrays as int32 / uint32.
 
 Each function names the page passage it follows; the C file holds the
@@ -28,6 +29,7 @@ _LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
 
 F32 = 0
 BF16 = 1
+F16 = 2
 GROUP_TOP2_SUM = 0
 GROUP_MAX = 1
 _ERRORS = {1: "invalid argument", 2: "input violates a precondition", 3: "out of memory"}
@@ -64,15 +66,17 @@ def _load():
         lib = ctypes.CDLL(path)
         p = ctypes.c_void_p
         i32, i64 = ctypes.c_int32, ctypes.c_int64
-        lib.moe_oracle_router.argtypes = [p, p, p, p, i64, i32, i32, i32, i32, i32,
+        lib.moe_oracle_router.argtypes = [p, p, p, p, i32, i32, i64, i32, i32, i32, i32, i32,
                                           ctypes.c_float, i32]
         lib.moe_oracle_router.restype = ctypes.c_int
         lib.moe_oracle_create_indices.argtypes = [p, p, p, p, p, p, i64, i32]
         lib.moe_oracle_create_indices.restype = ctypes.c_int
         lib.moe_oracle_finalize.argtypes = [p, i32, p, i32, p, p, i32, i64, i32, i64]
         lib.moe_oracle_finalize.restype = ctypes.c_int
-        lib.moe_oracle_f32_to_bf16_array.argtypes = [p, p, i64]
-        lib.moe_oracle_f32_to_bf16_array.restype = None
+        for fn in ("moe_oracle_f32_to_bf16_array", "moe_oracle_f32_to_f16_array",
+                   "moe_oracle_f16_to_f32_array"):
+            getattr(lib, fn).argtypes = [p, p, i64]
+            getattr(lib, fn).restype = None
         lib.moe_oracle_num_threads.argtypes = []
         lib.moe_oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -93,19 +97,31 @@ def num_threads() -> int:
     return int(_load().moe_oracle_num_threads())
 
 
+def _encoded(a, dtype):
+    """(contiguous array, dtype code): float32 arrays are F32; uint16 bit
+    patterns need an explicit BF16 or F16 code."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float32:
+        assert dtype in (None, F32)
+        return a, F32
+    assert a.dtype == np.uint16 and dtype in (BF16, F16), "uint16 data needs BF16 or F16"
+    return a, dtype
+
+
 def router(scores, bias, k: int, n_groups: int, topk_group: int, norm_weights: bool,
-           routed_scaling_factor: float, group_score: int = GROUP_TOP2_SUM):
+           routed_scaling_factor: float, group_score: int = GROUP_TOP2_SUM,
+           scores_dtype=None, bias_dtype=None):
     """Group-limited top-k router (group_limited_router_kernel page, description,
     Parameters and Args). Returns (expert_indices int32 [T, K],
-    expert_weights float32 [T, K])."""
-    s = np.ascontiguousarray(scores, dtype=np.float32)
-    b = np.ascontiguousarray(bias, dtype=np.float32)
+    expert_weights [T, K] in the scores' dtype)."""
+    s, sd = _encoded(scores, scores_dtype)
+    b, bd = _encoded(bias, bias_dtype)
     T, E = s.shape
     assert b.shape == (E,)
     idx = np.empty((T, k), dtype=np.int32)
-    w = np.empty((T, k), dtype=np.float32)
-    rc = _load().moe_oracle_router(_ptr(idx), _ptr(w), _ptr(s), _ptr(b), T, E, k, n_groups,
-                                   topk_group, int(bool(norm_weights)),
+    w = np.empty((T, k), dtype=np.float32 if sd == F32 else np.uint16)
+    rc = _load().moe_oracle_router(_ptr(idx), _ptr(w), _ptr(s), _ptr(b), sd, bd, T, E, k,
+                                   n_groups, topk_group, int(bool(norm_weights)),
                                    ctypes.c_float(routed_scaling_factor), group_score)
     _check(rc, "router")
     return idx, w
@@ -135,8 +151,9 @@ def create_indices(topk_ids, n_experts: int):
 def finalize(down, down_dtype: int, restore_order, router_weight, weight_dtype: int,
              out_dtype: int):
     """Fused unpermute gather plus weighted top-k sum (moe_finalize page,
-    description and Args). ``down`` is [T*K, H] (float32, or uint16 bf16 bits),
-    ``router_weight`` is [T, K]. Returns [T, H] float32 or uint16 bf16 bits."""
+    description and Args). ``down`` is [T*K, H] and ``router_weight`` [T, K]
+    (float32, or uint16 bit patterns for BF16 / F16). Returns [T, H] as float32
+    or uint16 bit patterns."""
     d = np.ascontiguousarray(down)
     w = np.ascontiguousarray(router_weight)
     r = np.ascontiguousarray(restore_order, dtype=np.uint32).reshape(-1)
@@ -164,3 +181,33 @@ def bf16_to_f32(bits) -> np.ndarray:
     """Widen bf16 bit patterns to float32 (exact)."""
     b = np.ascontiguousarray(bits, dtype=np.uint16)
     return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def f32_to_f16(x) -> np.ndarray:
+    """Round binary32 values to binary16 (nearest, ties to even); uint16 bits."""
+    a = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(a.shape, dtype=np.uint16)
+    _load().moe_oracle_f32_to_f16_array(_ptr(out), _ptr(a), a.size)
+    return out
+
+
+def f16_to_f32(bits) -> np.ndarray:
+    """Widen binary16 bit patterns to float32 (exact)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(b.shape, dtype=np.float32)
+    _load().moe_oracle_f16_to_f32_array(_ptr(out), _ptr(b), b.size)
+    return out
+
+
+def to_f32(bits, dtype: int) -> np.ndarray:
+    """Widen an array in dtype code `dtype` to float32."""
+    if dtype == F32:
+        return np.ascontiguousarray(bits, dtype=np.float32)
+    return bf16_to_f32(bits) if dtype == BF16 else f16_to_f32(bits)
+
+
+def from_f32(x, dtype: int) -> np.ndarray:
+    """Round float32 values to dtype code `dtype` (bit patterns for 16-bit)."""
+    if dtype == F32:
+        return np.ascontiguousarray(x, dtype=np.float32)
+    return f32_to_bf16(x) if dtype == BF16 else f32_to_f16(x)

@@ -44,7 +44,7 @@
 
 /* Oracle-local constants. They mirror nothing: the Python wrapper passes
  * these numbers explicitly. */
-enum { OR_F32 = 0, OR_BF16 = 1 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_F16 = 2 };
 enum { OR_GROUP_TOP2_SUM = 0, OR_GROUP_MAX = 1 };
 enum { OR_OK = 0, OR_BAD_ARG = 1, OR_BAD_DATA = 2, OR_NO_MEM = 3 };
 
@@ -86,10 +86,66 @@ void moe_oracle_f32_to_bf16_array(uint16_t* out, const float* in, int64_t n) {
     for (int64_t i = 0; i < n; ++i) out[i] = moe_oracle_f32_to_bf16(in[i]);
 }
 
+/* IEEE binary16 -> binary32, exact. */
+static float f16_bits_to_f32(uint16_t h) {
+    const uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
+    const uint32_t ex = (h >> 10) & 0x1fu;
+    const uint32_t man = h & 0x3ffu;
+    float f;
+    if (ex == 0) { /* zero or subnormal: man * 2^-24 */
+        f = ldexpf((float)man, -24);
+        return sign ? -f : f;
+    }
+    uint32_t u;
+    if (ex == 31)
+        u = sign | 0x7f800000u | (man << 13); /* infinity or NaN */
+    else
+        u = sign | ((ex + 112u) << 23) | (man << 13); /* rebias 15 -> 127 */
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* binary32 -> binary16, round to nearest, ties to even; overflow gives
+ * infinity, tiny values become subnormals or zero. */
+uint16_t moe_oracle_f32_to_f16(float f) {
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    const uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    const uint32_t a = u & 0x7fffffffu;
+    if (a > 0x7f800000u) return (uint16_t)(sign | 0x7e00u);  /* NaN */
+    if (a >= 0x477ff000u) return (uint16_t)(sign | 0x7c00u); /* >= 65520: infinity */
+    if (a < 0x38800000u) {                                   /* below 2^-14: subnormal */
+        const float scaled = fabsf(f) * 16777216.0f;          /* exact: times 2^24 */
+        return (uint16_t)(sign | (uint16_t)nearbyintf(scaled));
+    }
+    const uint32_t rounded = a + 0x0fffu + ((a >> 13) & 1u); /* nearest even at bit 13 */
+    return (uint16_t)(sign | ((rounded - 0x38000000u) >> 13));
+}
+
+void moe_oracle_f32_to_f16_array(uint16_t* out, const float* in, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = moe_oracle_f32_to_f16(in[i]);
+}
+
+void moe_oracle_f16_to_f32_array(float* out, const uint16_t* in, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = f16_bits_to_f32(in[i]);
+}
+
 static float load_as_f32(const void* p, int dtype, int64_t i) {
     if (dtype == OR_F32) return ((const float*)p)[i];
+    if (dtype == OR_F16) return f16_bits_to_f32(((const uint16_t*)p)[i]);
     return bf16_bits_to_f32(((const uint16_t*)p)[i]);
 }
+
+static void store_from_f32(void* p, int dtype, int64_t i, float v) {
+    if (dtype == OR_F32)
+        ((float*)p)[i] = v;
+    else if (dtype == OR_F16)
+        ((uint16_t*)p)[i] = moe_oracle_f32_to_f16(v);
+    else
+        ((uint16_t*)p)[i] = moe_oracle_f32_to_bf16(v);
+}
+
+static int dtype_ok(int d) { return d == OR_F32 || d == OR_BF16 || d == OR_F16; }
 
 /* ------------------------------------------------------------------ */
 /* Router (group_limited_router_kernel page)                          */
@@ -114,8 +170,11 @@ static int keyed_desc(const void* a, const void* b) {
 }
 
 /*
- * expert_indices [T, K] int32 and expert_weights [T, K] fp32 from
- * expert_scores [T, E] fp32 and expert_bias [E] fp32.
+ * expert_indices [T, K] int32 and expert_weights [T, K] from expert_scores
+ * [T, E] and expert_bias [E]. Scores and bias may be fp32, bf16 or fp16
+ * (scores_type and bias_type on the page); both are widened exactly to
+ * binary32. The weights are written in the scores' dtype (the page gives
+ * expert_weights the scores_type).
  *
  * Per token (router page, description):
  *  1. biased score b[e] = score[e] + bias[e], one binary32 add; the bias is
@@ -132,36 +191,39 @@ static int keyed_desc(const void* a, const void* b) {
  *  5. weights from the unbiased scores u_k = score[e_k]. With norm_weights
  *     they are divided by their sum before the scaling factor is applied
  *     (Parameters: norm_weights; Args: routed_scaling_factor). This step is
- *     evaluated in binary64 and rounded once to binary32.
+ *     evaluated in binary64, rounded to binary32, then to the output dtype.
  */
-int moe_oracle_router(int32_t* expert_indices, float* expert_weights,
-                      const float* scores, const float* bias,
-                      int64_t T, int32_t E, int32_t K, int32_t n_groups,
-                      int32_t topk_group, int32_t norm_weights,
-                      float routed_scaling_factor, int32_t group_score) {
+int moe_oracle_router(int32_t* expert_indices, void* expert_weights, const void* scores,
+                      const void* bias, int32_t scores_dtype, int32_t bias_dtype, int64_t T,
+                      int32_t E, int32_t K, int32_t n_groups, int32_t topk_group,
+                      int32_t norm_weights, float routed_scaling_factor, int32_t group_score) {
     if (T < 0 || E <= 0 || n_groups <= 0 || E % n_groups != 0) return OR_BAD_ARG;
     if (topk_group < 1 || topk_group > n_groups) return OR_BAD_ARG;
     const int32_t S = E / n_groups;
     if (K < 1 || K > topk_group * S) return OR_BAD_ARG;
     if (group_score != OR_GROUP_TOP2_SUM && group_score != OR_GROUP_MAX) return OR_BAD_ARG;
+    if (!dtype_ok(scores_dtype) || !dtype_ok(bias_dtype)) return OR_BAD_ARG;
 
     int rc = OR_OK;
 #pragma omp parallel
     {
+        float* s = (float*)malloc(sizeof(float) * (size_t)E);
         float* b = (float*)malloc(sizeof(float) * (size_t)E);
         keyed_t* grp = (keyed_t*)malloc(sizeof(keyed_t) * (size_t)S);
         keyed_t* gsc = (keyed_t*)malloc(sizeof(keyed_t) * (size_t)n_groups);
         keyed_t* cand = (keyed_t*)malloc(sizeof(keyed_t) * (size_t)E);
         char* kept = (char*)malloc((size_t)n_groups);
-        if (!b || !grp || !gsc || !cand || !kept) {
+        if (!s || !b || !grp || !gsc || !cand || !kept) {
 #pragma omp atomic write
             rc = OR_NO_MEM;
         } else {
 #pragma omp for schedule(static)
             for (int64_t t = 0; t < T; ++t) {
-                const float* s = scores + t * (int64_t)E;
                 /* 1. biased scores */
-                for (int32_t e = 0; e < E; ++e) b[e] = s[e] + bias[e];
+                for (int32_t e = 0; e < E; ++e) {
+                    s[e] = load_as_f32(scores, scores_dtype, t * (int64_t)E + e);
+                    b[e] = s[e] + load_as_f32(bias, bias_dtype, e);
+                }
                 /* 2. group scores */
                 for (int32_t g = 0; g < n_groups; ++g) {
                     for (int32_t j = 0; j < S; ++j) {
@@ -197,10 +259,11 @@ int moe_oracle_router(int32_t* expert_indices, float* expert_weights,
                     if (norm_weights) w = w / sum;
                     w = w * (double)routed_scaling_factor;
                     expert_indices[t * K + k] = e;
-                    expert_weights[t * K + k] = (float)w;
+                    store_from_f32(expert_weights, scores_dtype, t * K + k, (float)w);
                 }
             }
         }
+        free(s);
         free(b);
         free(grp);
         free(gsc);
@@ -295,17 +358,16 @@ int moe_oracle_create_indices(uint32_t* token_expert_order, uint32_t* expert_sta
  * accumulated in binary32 (the page: "accumulates in fp32"), starting from
  * +0 and adding the K terms in k order, each term fused into the running
  * sum by one correctly rounded fmaf. The accumulator is then stored as
- * out_type (bf16 by round to nearest even). down, router_weight and output
- * may each be fp32 or bf16 (down_type, weight_type, out_type on the page).
+ * out_type (bf16 and fp16 by round to nearest even). down, router_weight
+ * and output may each be fp32, bf16 or fp16 (down_type, weight_type,
+ * out_type on the page).
  * restore_order entries must lie in [0, T*K).
  */
 int moe_oracle_finalize(void* output, int32_t out_dtype, const void* down, int32_t down_dtype,
                         const uint32_t* restore_order, const void* router_weight,
                         int32_t weight_dtype, int64_t T, int32_t K, int64_t H) {
     if (T < 0 || K < 1 || H < 0) return OR_BAD_ARG;
-    if ((out_dtype != OR_F32 && out_dtype != OR_BF16) ||
-        (down_dtype != OR_F32 && down_dtype != OR_BF16) ||
-        (weight_dtype != OR_F32 && weight_dtype != OR_BF16))
+    if (!dtype_ok(out_dtype) || !dtype_ok(down_dtype) || !dtype_ok(weight_dtype))
         return OR_BAD_ARG;
     const int64_t N = T * (int64_t)K;
     for (int64_t i = 0; i < N; ++i)
@@ -328,12 +390,7 @@ int moe_oracle_finalize(void* output, int32_t out_dtype, const void* down, int32
                     for (int64_t h = 0; h < H; ++h)
                         acc[h] = fmaf(w, load_as_f32(down, down_dtype, row * H + h), acc[h]);
                 }
-                for (int64_t h = 0; h < H; ++h) {
-                    if (out_dtype == OR_F32)
-                        ((float*)output)[t * H + h] = acc[h];
-                    else
-                        ((uint16_t*)output)[t * H + h] = moe_oracle_f32_to_bf16(acc[h]);
-                }
+                for (int64_t h = 0; h < H; ++h) store_from_f32(output, out_dtype, t * H + h, acc[h]);
             }
         }
         free(acc);

@@ -7,6 +7,7 @@ the library must share).
 """
 from .binding import (  # noqa: F401
     DTYPE_BF16,
+    DTYPE_F16,
     DTYPE_F32,
     GROUP_MAX,
     GROUP_TOP2_SUM,

@@ -23,6 +23,7 @@ _LIB_PATH = os.path.join(_HERE, "libmoe_route.so")
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
+DTYPE_F16 = 2
 GROUP_TOP2_SUM = 0
 GROUP_MAX = 1
 
@@ -98,7 +99,9 @@ def _dtype_code(t: torch.Tensor) -> int:
         return DTYPE_F32
     if t.dtype == torch.bfloat16:
         return DTYPE_BF16
-    raise TypeError("unsupported dtype %s (float32 or bfloat16)" % t.dtype)
+    if t.dtype == torch.float16:
+        return DTYPE_F16
+    raise TypeError("unsupported dtype %s (float32, bfloat16 or float16)" % t.dtype)
 
 
 def _ptr(t):

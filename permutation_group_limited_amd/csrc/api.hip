@@ -12,7 +12,13 @@ thread_local int g_last_hip_error = 0;
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 size_t dtype_bytes(moe_dtype_t d) { return d == MOE_DTYPE_F32 ? 4 : 2; }
-bool dtype_ok(moe_dtype_t d) { return d == MOE_DTYPE_F32 || d == MOE_DTYPE_BF16; }
+bool dtype_ok(moe_dtype_t d) {
+  return d == MOE_DTYPE_F32 || d == MOE_DTYPE_BF16 || d == MOE_DTYPE_F16;
+}
+// score/bias dtype pairs with a router instance: equal, or fp32 bias
+bool router_dtypes_supported(moe_dtype_t s, moe_dtype_t b) {
+  return s == b || b == MOE_DTYPE_F32;
+}
 }  // namespace
 
 moe_status_t hip_failure(hipError_t err) {
@@ -49,17 +55,16 @@ moe_status_t moe_router_group_limited(int32_t* expert_indices, void* expert_weig
   if (T > 0 && (!expert_indices || !expert_weights || !expert_scores || !expert_bias))
     return MOE_ERR_INVALID_ARG;
   if (T > (int64_t)UINT32_MAX / K) return MOE_ERR_INVALID_ARG;
-  if (scores_dtype != MOE_DTYPE_F32 || bias_dtype != MOE_DTYPE_F32) return MOE_ERR_UNSUPPORTED;
+  if (!router_dtypes_supported(scores_dtype, bias_dtype)) return MOE_ERR_UNSUPPORTED;
   if (!is_pow2(E) || E > 1024) return MOE_ERR_UNSUPPORTED;
   if (!aligned(expert_scores, 16) || !aligned(expert_bias, 16) || !aligned(expert_indices, 4) ||
-      !aligned(expert_weights, 4))
+      !aligned(expert_weights, dtype_bytes(scores_dtype)))
     return MOE_ERR_ALIGNMENT;
   if (T == 0) return MOE_OK;
-  return launch_router(expert_indices, static_cast<float*>(expert_weights),
-                       static_cast<const float*>(expert_scores),
-                       static_cast<const float*>(expert_bias), T, E, K, n_groups, topk_group,
-                       norm_weights ? 1 : 0, routed_scaling_factor,
-                       static_cast<int32_t>(group_score), static_cast<hipStream_t>(stream));
+  return launch_router(expert_indices, expert_weights, expert_scores, expert_bias, scores_dtype,
+                       bias_dtype, T, E, K, n_groups, topk_group, norm_weights ? 1 : 0,
+                       routed_scaling_factor, static_cast<int32_t>(group_score),
+                       static_cast<hipStream_t>(stream));
 }
 
 size_t moe_create_indices_workspace_size(int64_t N, int32_t E) {

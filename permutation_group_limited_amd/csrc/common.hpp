@@ -2,8 +2,8 @@
 //
 // Everything here is CDNA wave64 code: 64-lane wavefronts, 64-bit ballots,
 // cross-lane traffic through ds_bpermute / DPP (via the HIP shuffle
-// intrinsics), bf16 conversion by the gfx950 hardware converter
-// (v_cvt_pk_bf16_f32, round to nearest even).
+// intrinsics), bf16 / fp16 conversion by the gfx950 hardware converters
+// (round to nearest even).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -21,14 +21,43 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
-  return __uint_as_float(h << 16);
-}
+// ---- element types -------------------------------------------------------
+// Storage tags for the three dtypes of the ABI. Widening to fp32 is exact;
+// narrowing rounds to nearest even (gfx950 v_cvt_pk_bf16_f32 and
+// v_cvt_f16_f32).
+struct DF32 {
+  using storage = float;
+  static constexpr int kBytes = 4;
+  __device__ static __forceinline__ float widen_bits(uint32_t b) { return __uint_as_float(b); }
+  __device__ static __forceinline__ uint32_t narrow_bits(float f) { return __float_as_uint(f); }
+};
+struct DBF16 {
+  using storage = uint16_t;
+  static constexpr int kBytes = 2;
+  __device__ static __forceinline__ float widen_bits(uint32_t b) { return __uint_as_float(b << 16); }
+  // element held in the high half of a 32-bit word
+  __device__ static __forceinline__ float widen_hi(uint32_t w) {
+    return __uint_as_float(w & 0xFFFF0000u);
+  }
+  __device__ static __forceinline__ uint32_t narrow_bits(float f) {
+    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(f)));
+  }
+};
+struct DF16 {
+  using storage = uint16_t;
+  static constexpr int kBytes = 2;
+  __device__ static __forceinline__ float widen_bits(uint32_t b) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b)));
+  }
+  __device__ static __forceinline__ float widen_hi(uint32_t w) { return widen_bits(w >> 16); }
+  __device__ static __forceinline__ uint32_t narrow_bits(float f) {
+    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(f)));
+  }
+};
 
-// fp32 -> bf16 bits, round to nearest even (hardware conversion on gfx950).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  __bf16 b = static_cast<__bf16>(f);
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b));
+template <typename D>
+__device__ __forceinline__ float load_f32(const typename D::storage* p, int64_t i) {
+  return D::widen_bits(static_cast<uint32_t>(p[i]));
 }
 
 // Monotone map binary32 -> uint32 for finite inputs: a < b  <=>  key(a) <
@@ -68,10 +97,10 @@ __device__ __forceinline__ uint64_t match_any(uint32_t key, int nbits, uint64_t 
 
 // ---- launchers (host side), one per stage --------------------------------
 
-moe_status_t launch_router(int32_t* expert_indices, float* expert_weights, const float* scores,
-                           const float* bias, int64_t T, int32_t E, int32_t K, int32_t n_groups,
-                           int32_t topk_group, int32_t norm_weights, float scale, int32_t mode,
-                           hipStream_t stream);
+moe_status_t launch_router(int32_t* expert_indices, void* expert_weights, const void* scores,
+                           const void* bias, moe_dtype_t scores_dtype, moe_dtype_t bias_dtype,
+                           int64_t T, int32_t E, int32_t K, int32_t n_groups, int32_t topk_group,
+                           int32_t norm_weights, float scale, int32_t mode, hipStream_t stream);
 
 struct IndexPlan {
   int waves;        // waves per workgroup (16 when E <= 256, else 4)

@@ -27,24 +27,43 @@
 namespace moe {
 namespace {
 
-template <int EPL>
-__device__ __forceinline__ void load_row(float (&dst)[EPL], const float* __restrict__ p) {
-  if constexpr (EPL % 4 == 0) {
-#pragma unroll
-    for (int i = 0; i < EPL; i += 4) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(p + i);
-      dst[i] = v.x;
-      dst[i + 1] = v.y;
-      dst[i + 2] = v.z;
-      dst[i + 3] = v.w;
-    }
-  } else if constexpr (EPL == 2) {
-    const float2 v = *reinterpret_cast<const float2*>(p);
-    dst[0] = v.x;
-    dst[1] = v.y;
+// Load EPL consecutive elements of dtype D (one vector load of EPL * size
+// bytes when that is 4, 8 or a multiple of 16) and widen them to fp32.
+template <typename D, int EPL>
+__device__ __forceinline__ void load_row(float (&dst)[EPL],
+                                         const typename D::storage* __restrict__ p) {
+  constexpr int kBytes = EPL * D::kBytes;
+  if constexpr (kBytes == 2) {
+    dst[0] = D::widen_bits(static_cast<uint32_t>(p[0]));
   } else {
+    constexpr int kWords = kBytes / 4;
+    uint32_t w[kWords];
+    if constexpr (kBytes % 16 == 0) {
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) dst[i] = p[i];
+      for (int q = 0; q < kWords; q += 4) {
+        const u32x4 v = reinterpret_cast<const u32x4*>(p)[q / 4];
+        w[q] = v.x;
+        w[q + 1] = v.y;
+        w[q + 2] = v.z;
+        w[q + 3] = v.w;
+      }
+    } else if constexpr (kBytes == 8) {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+      w[0] = v.x;
+      w[1] = v.y;
+    } else {
+      w[0] = *reinterpret_cast<const uint32_t*>(p);
+    }
+    if constexpr (D::kBytes == 4) {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) dst[i] = D::widen_bits(w[i]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < kWords; ++q) {
+        dst[2 * q] = D::widen_bits(w[q] & 0xFFFFu);
+        dst[2 * q + 1] = D::widen_hi(w[q]);
+      }
+    }
   }
 }
 
@@ -145,11 +164,12 @@ __device__ __forceinline__ void sort_desc(uint32_t (&k)[EPL], uint32_t (&e)[EPL]
   }
 }
 
-template <int EPL, int LPT>
+template <typename DS, typename DB, int EPL, int LPT>
 __global__ __launch_bounds__(kBlock) void router_kernel(
-    int32_t* __restrict__ out_idx, float* __restrict__ out_w, const float* __restrict__ scores,
-    const float* __restrict__ bias, int64_t T, int32_t K, int32_t n_groups, int32_t topk_group,
-    int32_t norm_weights, float scale, int32_t mode) {
+    int32_t* __restrict__ out_idx, typename DS::storage* __restrict__ out_w,
+    const typename DS::storage* __restrict__ scores, const typename DB::storage* __restrict__ bias,
+    int64_t T, int32_t K, int32_t n_groups, int32_t topk_group, int32_t norm_weights,
+    float scale, int32_t mode) {
   constexpr int E = EPL * LPT;
   constexpr int TPW = kWave / LPT;  // tokens per wave
   const int lane = lane_id();
@@ -165,12 +185,12 @@ __global__ __launch_bounds__(kBlock) void router_kernel(
 
   float s[EPL], bi[EPL], b[EPL];
   if (tok_ok) {
-    load_row<EPL>(s, scores + t * E + e0);
+    load_row<DS, EPL>(s, scores + t * E + e0);
   } else {
 #pragma unroll
     for (int i = 0; i < EPL; ++i) s[i] = 0.0f;
   }
-  load_row<EPL>(bi, bias + e0);
+  load_row<DB, EPL>(bi, bias + e0);
 #pragma unroll
   for (int i = 0; i < EPL; ++i) b[i] = s[i] + bi[i];
 
@@ -244,7 +264,7 @@ __global__ __launch_bounds__(kBlock) void router_kernel(
   // ---- weights from the unbiased scores -----------------------------------
   const bool slot = tok_ok && sub < K;
   if (my_id >= static_cast<uint32_t>(E)) my_id = 0;  // unreachable with finite scores
-  const float u = slot ? scores[t * E + my_id] : 0.0f;
+  const float u = slot ? load_f32<DS>(scores, t * E + my_id) : 0.0f;
   float w;
   if (norm_weights) {
     float d = 0.0f;
@@ -260,40 +280,63 @@ __global__ __launch_bounds__(kBlock) void router_kernel(
   }
   if (slot) {
     out_idx[t * K + sub] = static_cast<int32_t>(my_id);
-    out_w[t * K + sub] = w;
+    out_w[t * K + sub] = static_cast<typename DS::storage>(DS::narrow_bits(w));
   }
 }
 
-template <int EPL, int LPT>
-moe_status_t launch_router_t(int32_t* idx, float* w, const float* s, const float* b, int64_t T,
+template <typename DS, typename DB, int EPL, int LPT>
+moe_status_t launch_router_t(int32_t* idx, void* w, const void* s, const void* b, int64_t T,
                              int32_t K, int32_t G, int32_t TG, int32_t norm, float scale,
                              int32_t mode, hipStream_t stream) {
   constexpr int TPB = kWavesPerBlock * (kWave / LPT);  // tokens per block
   const int64_t blocks = (T + TPB - 1) / TPB;
-  hipLaunchKernelGGL((router_kernel<EPL, LPT>), dim3(static_cast<uint32_t>(blocks)), dim3(kBlock),
-                     0, stream, idx, w, s, b, T, K, G, TG, norm, scale, mode);
+  hipLaunchKernelGGL((router_kernel<DS, DB, EPL, LPT>), dim3(static_cast<uint32_t>(blocks)),
+                     dim3(kBlock), 0, stream, idx, static_cast<typename DS::storage*>(w),
+                     static_cast<const typename DS::storage*>(s),
+                     static_cast<const typename DB::storage*>(b), T, K, G, TG, norm, scale, mode);
   return check_launch();
+}
+
+template <typename DS, typename DB>
+moe_status_t launch_router_e(int32_t* idx, void* w, const void* s, const void* b, int64_t T,
+                             int32_t E, int32_t K, int32_t G, int32_t TG, int32_t norm,
+                             float scale, int32_t mode, hipStream_t stream) {
+#define MOE_R(EPL, LPT) \
+  return launch_router_t<DS, DB, EPL, LPT>(idx, w, s, b, T, K, G, TG, norm, scale, mode, stream)
+  switch (E) {
+    case 1: MOE_R(1, 1);
+    case 2: MOE_R(1, 2);
+    case 4: MOE_R(1, 4);
+    case 8: MOE_R(1, 8);
+    case 16: MOE_R(1, 16);
+    case 32: MOE_R(1, 32);
+    case 64: MOE_R(1, 64);
+    case 128: MOE_R(2, 64);
+    case 256: MOE_R(4, 64);
+    case 512: MOE_R(8, 64);
+    case 1024: MOE_R(16, 64);
+    default: return MOE_ERR_UNSUPPORTED;
+  }
+#undef MOE_R
 }
 
 }  // namespace
 
-moe_status_t launch_router(int32_t* idx, float* w, const float* s, const float* b, int64_t T,
-                           int32_t E, int32_t K, int32_t G, int32_t TG, int32_t norm, float scale,
-                           int32_t mode, hipStream_t stream) {
-  switch (E) {
-    case 1: return launch_router_t<1, 1>(idx, w, s, b, T, K, G, TG, norm, scale, mode, stream);
-    case 2: return launch_router_t<1, 2>(idx, w, s, b, T, K, G, TG, norm, scale, mode, stream);
-    case 4: return launch_router_t<1, 4>(idx, w, s, b, T, K, G, TG, norm, scale, mode, stream);
-    case 8: return launch_router_t<1, 8>(idx, w, s, b, T, K, G, TG, norm, scale, mode, stream);
-    case 16: return launch_router_t<1, 16>(idx, w, s, b, T, K, G, TG, norm, scale, mode, stream);
-    case 32: return launch_router_t<1, 32>(idx, w, s, b, T, K, G, TG, norm, scale, mode, stream);
-    case 64: return launch_router_t<1, 64>(idx, w, s, b, T, K, G, TG, norm, scale, mode, stream);
-    case 128: return launch_router_t<2, 64>(idx, w, s, b, T, K, G, TG, norm, scale, mode, stream);
-    case 256: return launch_router_t<4, 64>(idx, w, s, b, T, K, G, TG, norm, scale, mode, stream);
-    case 512: return launch_router_t<8, 64>(idx, w, s, b, T, K, G, TG, norm, scale, mode, stream);
-    case 1024: return launch_router_t<16, 64>(idx, w, s, b, T, K, G, TG, norm, scale, mode, stream);
-    default: return MOE_ERR_UNSUPPORTED;
-  }
+moe_status_t launch_router(int32_t* idx, void* w, const void* s, const void* b,
+                           moe_dtype_t sd, moe_dtype_t bd, int64_t T, int32_t E, int32_t K,
+                           int32_t G, int32_t TG, int32_t norm, float scale, int32_t mode,
+                           hipStream_t stream) {
+  if (sd == MOE_DTYPE_F32 && bd == MOE_DTYPE_F32)
+    return launch_router_e<DF32, DF32>(idx, w, s, b, T, E, K, G, TG, norm, scale, mode, stream);
+  if (sd == MOE_DTYPE_BF16 && bd == MOE_DTYPE_BF16)
+    return launch_router_e<DBF16, DBF16>(idx, w, s, b, T, E, K, G, TG, norm, scale, mode, stream);
+  if (sd == MOE_DTYPE_BF16 && bd == MOE_DTYPE_F32)
+    return launch_router_e<DBF16, DF32>(idx, w, s, b, T, E, K, G, TG, norm, scale, mode, stream);
+  if (sd == MOE_DTYPE_F16 && bd == MOE_DTYPE_F16)
+    return launch_router_e<DF16, DF16>(idx, w, s, b, T, E, K, G, TG, norm, scale, mode, stream);
+  if (sd == MOE_DTYPE_F16 && bd == MOE_DTYPE_F32)
+    return launch_router_e<DF16, DF32>(idx, w, s, b, T, E, K, G, TG, norm, scale, mode, stream);
+  return MOE_ERR_UNSUPPORTED;
 }
 
 }  // namespace moe

@@ -8,8 +8,9 @@ Acceptance:
   * finalize, fp32 output: |gpu - oracle| <= 1e-5 * sum_k |w_k * down_k|
     (relative to the magnitude of the terms, so cancellation cannot fail a
     correct result);
-  * finalize, bf16 output: at most 1 bf16 ulp apart (ordered bit patterns,
-    +0 and -0 equal);
+  * finalize, bf16 / fp16 output: at most 1 ulp apart (ordered bit
+    patterns, +0 and -0 equal); router weights stored in bf16 / fp16 the
+    same;
   * the chained pipeline feeds finalize the GPU's own weights, which may
     differ from the oracle's within the router tolerance (1e-6 relative);
     there the bound is (1e-6 + 2*K*2^-24) * sum_k |w_k d_k| (that weight
@@ -39,18 +40,43 @@ def to_np_u32(t: torch.Tensor) -> np.ndarray:
 
 
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    """16-bit float tensor (bf16 or fp16) -> uint16 bit patterns."""
     return t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
 
 
+def oracle_code(dtype) -> int:
+    return {torch.float32: oracle.F32, torch.bfloat16: oracle.BF16,
+            torch.float16: oracle.F16}[dtype]
+
+
+def encode(t: torch.Tensor):
+    """Host tensor -> (numpy array for the oracle, dtype code)."""
+    if t.dtype == torch.float32:
+        return t.contiguous().numpy(), oracle.F32
+    return bf16_bits(t), oracle_code(t.dtype)
+
+
+def assert_16bit_within_one_ulp(got_bits, exp_bits, what):
+    g = _bf16_ordered(np.asarray(got_bits, np.uint16))
+    e = _bf16_ordered(np.asarray(exp_bits, np.uint16))
+    d = np.abs(g - e)
+    if d.max(initial=0) > 1:
+        i = np.argwhere(d > 1)[:5]
+        raise AssertionError("%s more than 1 ulp off at %s" % (what, i.tolist()))
+
+
 def gpu_router(scores, bias, K, G, TG, norm, scale, mode=0):
+    """Router on the GPU; weights come back as a host tensor in the scores'
+    dtype (numpy float32 for fp32 scores)."""
     T, E = scores.shape
     s = scores.to(DEV)
     b = bias.to(DEV)
     idx = torch.full((T, K), -7, dtype=torch.int32, device=DEV)
-    w = torch.full((T, K), float("nan"), dtype=torch.float32, device=DEV)
+    w = torch.full((T, K), float("nan"), dtype=scores.dtype, device=DEV)
     binding.moe_router_group_limited(idx, w, s, b, G, TG, norm, scale, mode)
     torch.cuda.synchronize()
-    return idx.cpu().numpy(), w.cpu().numpy()
+    wh = w.cpu()
+    return idx.cpu().numpy(), (wh.numpy() if wh.dtype == torch.float32 else wh)
 
 
 def gpu_indices(ids, E, poison=True):
@@ -88,15 +114,11 @@ def gpu_finalize(down_dev, restore, weight, out_dtype):
 
 
 def oracle_finalize_from(down_host, restore, weight, out_dtype):
-    """Oracle finalize on host tensors (down/weight float32 or bfloat16)."""
-    def enc(t):
-        if t.dtype == torch.bfloat16:
-            return bf16_bits(t), oracle.BF16
-        return t.contiguous().numpy(), oracle.F32
-    d, dd = enc(down_host)
-    w, wd = enc(weight)
-    od = oracle.BF16 if out_dtype == torch.bfloat16 else oracle.F32
-    return oracle.finalize(d, dd, np.asarray(restore, dtype=np.uint32), w, wd, od)
+    """Oracle finalize on host tensors (float32, bfloat16 or float16)."""
+    d, dd = encode(down_host)
+    w, wd = encode(weight)
+    return oracle.finalize(d, dd, np.asarray(restore, dtype=np.uint32), w, wd,
+                           oracle_code(out_dtype))
 
 
 def term_magnitude(down_host, restore, weight):
@@ -135,11 +157,12 @@ def _bf16_ordered(bits: np.ndarray) -> np.ndarray:
     return np.where(b & 0x8000, -mag, mag)
 
 
-def bf16_spacing(x: np.ndarray) -> np.ndarray:
-    """Distance from |x| to the next bf16 value away from zero (x in float64)."""
+def spacing16(x: np.ndarray, code: int) -> np.ndarray:
+    """Distance from |x| to the next bf16 / fp16 value away from zero."""
+    mant, emin = (7, -126) if code == oracle.BF16 else (10, -14)
     a = np.abs(x)
     e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
-    return np.where(a > 0, np.exp2(np.maximum(e, -126.0) - 7.0), 2.0 ** -133)
+    return np.exp2(np.maximum(np.where(a > 0, e, emin), emin) - mant)
 
 
 def assert_finalize_close(got_dev, exp_np, mag, weight_rel_tol=0.0):
@@ -147,14 +170,15 @@ def assert_finalize_close(got_dev, exp_np, mag, weight_rel_tol=0.0):
     where the GPU's weights may differ from the oracle's by the router's
     tolerance) an output also passes when it is within weight_rel_tol *
     sum_k |w_k d_k| plus one bf16 spacing of the oracle's."""
-    if got_dev.dtype == torch.bfloat16:
+    if got_dev.dtype in (torch.bfloat16, torch.float16):
+        code = oracle_code(got_dev.dtype)
         gb, eb = bf16_bits(got_dev), np.asarray(exp_np, np.uint16)
         diff = np.abs(_bf16_ordered(gb) - _bf16_ordered(eb))
         bad = diff > 1
         if weight_rel_tol > 0 and bad.any():
-            gf = oracle.bf16_to_f32(gb).astype(np.float64)
-            ef = oracle.bf16_to_f32(eb).astype(np.float64)
-            spacing = bf16_spacing(np.maximum(np.abs(gf), np.abs(ef)))
+            gf = oracle.to_f32(gb, code).astype(np.float64)
+            ef = oracle.to_f32(eb, code).astype(np.float64)
+            spacing = spacing16(np.maximum(np.abs(gf), np.abs(ef)), code)
             bad &= np.abs(gf - ef) > weight_rel_tol * mag + spacing
         if bad.any():
             i = np.argwhere(bad)[:5]

@@ -65,7 +65,8 @@ def router(lib, T=4, E=256, K=8, G=8, TG=4, norm=1, mode=0, ptrs=None, sd=0, bd=
     (dict(G=128, E=256, TG=4), INVALID), (dict(TG=0), INVALID), (dict(TG=9), INVALID),
     (dict(K=0), INVALID), (dict(K=129, TG=4), INVALID), (dict(E=256, G=8, TG=1, K=33), INVALID),
     (dict(E=1024, G=1, TG=1, K=65), INVALID), (dict(mode=2), INVALID), (dict(sd=7), INVALID),
-    (dict(sd=1), UNSUPPORTED), (dict(bd=1), UNSUPPORTED), (dict(E=96, G=8, TG=4), UNSUPPORTED),
+    (dict(sd=1, bd=2), UNSUPPORTED), (dict(bd=1), UNSUPPORTED), (dict(sd=2, bd=1), UNSUPPORTED),
+    (dict(E=96, G=8, TG=4), UNSUPPORTED),
     (dict(E=2048, G=8, TG=4), UNSUPPORTED),
     (dict(ptrs=(None, FAKE, FAKE, FAKE)), INVALID),
     (dict(ptrs=(FAKE, FAKE, FAKE_MIS, FAKE)), ALIGNMENT),
@@ -107,8 +108,9 @@ def finalize(lib, T=4, K=2, H=64, od=1, dd=1, wd=0, ptrs=None):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(T=-1), INVALID), (dict(K=0), INVALID), (dict(H=-8), INVALID), (dict(od=3), INVALID),
-    (dict(dd=2), INVALID), (dict(T=1 << 31, K=2), INVALID),
+    (dict(dd=3), INVALID), (dict(wd=-1), INVALID), (dict(T=1 << 31, K=2), INVALID),
     (dict(H=12, dd=1), ALIGNMENT),  # 24-byte rows
+    (dict(H=20, dd=2), ALIGNMENT),  # 40-byte rows
     (dict(H=6, dd=0), ALIGNMENT),
     (dict(ptrs=(FAKE_MIS, FAKE, FAKE, FAKE)), ALIGNMENT),
     (dict(ptrs=(FAKE, FAKE, FAKE, None)), INVALID),

@@ -13,7 +13,7 @@ from _gpu import (DEV, assert_finalize_close, gpu_finalize, log, oracle_finalize
 
 pytestmark = pytest.mark.gpu
 
-DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 def _inputs(T, K, H, ddt, wdt, seed):
@@ -24,13 +24,13 @@ def _inputs(T, K, H, ddt, wdt, seed):
     return down, w, restore
 
 
-@pytest.mark.parametrize("ddt", ["f32", "bf16"])
-@pytest.mark.parametrize("wdt", ["f32", "bf16"])
-@pytest.mark.parametrize("odt", ["f32", "bf16"])
+@pytest.mark.parametrize("ddt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("wdt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("odt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("T,K,H", [(1, 1, 8), (5, 2, 136), (33, 8, 520), (17, 3, 1032),
                                    (9, 9, 264), (4, 16, 64), (40, 6, 7168), (3, 1, 4096)])
 def test_random_shapes(ddt, wdt, odt, T, K, H):
-    if ddt == "f32" and H % 4 or ddt == "bf16" and H % 8:
+    if ddt == "f32" and H % 4 or ddt != "f32" and H % 8:
         pytest.skip("row not a multiple of 16 bytes")
     log("finalize case", ddt, wdt, odt, T, K, H)
     down, w, restore = _inputs(T, K, H, DT[ddt], DT[wdt], seed=T * 100 + K * 10 + H)

@@ -8,7 +8,8 @@ import torch
 import oracle
 from permutation_group_limited_amd import workloads as wl
 
-from _gpu import assert_weights_close, gpu_router, log
+from _gpu import (assert_16bit_within_one_ulp, assert_weights_close, bf16_bits, encode,
+                  gpu_router, log)
 
 pytestmark = pytest.mark.gpu
 
@@ -86,3 +87,24 @@ def test_deterministic():
         c = gpu_router(s, b, 8, 8, 4, True, 2.5)
         assert np.array_equal(a[0], c[0]) and np.array_equal(a[1].view(np.uint32),
                                                              c[1].view(np.uint32))
+
+
+DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+@pytest.mark.parametrize("sd,bd", [("bf16", "bf16"), ("bf16", "f32"), ("f16", "f16"),
+                                   ("f16", "f32")])
+@pytest.mark.parametrize("T,E,G,TG,K", [(300, 256, 8, 4, 8), (129, 8, 1, 1, 2),
+                                        (77, 64, 8, 3, 6), (65, 1024, 16, 4, 8)])
+def test_16bit_scores(sd, bd, T, E, G, TG, K):
+    log("router dtypes", sd, bd, T, E, G, TG, K)
+    for levels in (0, 3):
+        s = wl.random_scores(T, E, seed=E + T, levels=levels).to(DTYPES[sd])
+        b = wl.random_bias(E, seed=G, std=0.02, levels=levels).to(DTYPES[bd])
+        gi, gw = gpu_router(s, b, K, G, TG, True, 2.5)
+        sn, scode = encode(s)
+        bn, bcode = encode(b)
+        oi, ow = oracle.router(sn, bn, K, G, TG, True, 2.5, scores_dtype=scode,
+                               bias_dtype=None if bd == "f32" else bcode)
+        assert np.array_equal(gi, oi)
+        assert_16bit_within_one_ulp(bf16_bits(gw), ow, "router weights")

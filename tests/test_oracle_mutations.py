@@ -19,7 +19,7 @@ FINALIZE = "tests/test_oracle_finalize.py"
 
 MUTATIONS = [
     ("bias left out of the selection", ROUTER,
-     "b[e] = s[e] + bias[e];", "b[e] = s[e];"),
+     "b[e] = s[e] + load_as_f32(bias, bias_dtype, e);", "b[e] = s[e];"),
     ("bias added into the weights", ROUTER,
      "double w = (double)s[e];", "double w = (double)b[e];"),
     ("group score is the maximum only", ROUTER,
