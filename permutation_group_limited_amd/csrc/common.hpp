@@ -55,9 +55,23 @@ struct DF16 {
   }
 };
 
+// Element i of p widened to fp32, and an fp32 value rounded to D's storage
+// (bit patterns for the 16-bit types, the value itself for fp32).
 template <typename D>
 __device__ __forceinline__ float load_f32(const typename D::storage* p, int64_t i) {
-  return D::widen_bits(static_cast<uint32_t>(p[i]));
+  if constexpr (D::kBytes == 4) {
+    return p[i];
+  } else {
+    return D::widen_bits(static_cast<uint32_t>(p[i]));
+  }
+}
+template <typename D>
+__device__ __forceinline__ typename D::storage to_storage(float f) {
+  if constexpr (D::kBytes == 4) {
+    return f;
+  } else {
+    return static_cast<typename D::storage>(D::narrow_bits(f));
+  }
 }
 
 // Monotone map binary32 -> uint32 for finite inputs: a < b  <=>  key(a) <

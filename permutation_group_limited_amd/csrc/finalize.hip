@@ -65,14 +65,6 @@ __device__ __forceinline__ void store_out(typename D::storage* p, const float* a
   }
 }
 
-// Router weight k of the wave's token, widened to fp32. The dtype is a
-// uniform run-time value; the load is wave-uniform (scalar path).
-__device__ __forceinline__ float load_weight(const void* w, moe_dtype_t wd, int64_t i) {
-  if (wd == MOE_DTYPE_F32) return static_cast<const float*>(w)[i];
-  const uint32_t b = static_cast<const uint16_t*>(w)[i];
-  return wd == MOE_DTYPE_BF16 ? DBF16::widen_bits(b) : DF16::widen_bits(b);
-}
-
 // KB: rows gathered per batch of loads. EXACT: K == KB, so the whole
 // reduction is one batch with no bounds tests (K <= 8); otherwise batches of
 // KB rows with a ragged last batch.
@@ -100,31 +92,40 @@ __global__ __launch_bounds__(kBlock) void finalize_kernel(
   const int32_t k_end = EXACT ? KB : K;
   for (int32_t kb = 0; kb < k_end; kb += KB) {
     const int nb = EXACT ? KB : ((k_end - kb) < KB ? (k_end - kb) : KB);
+    // restore entries first (one batched scalar load), then every row load,
+    // then the weights, so that all K row loads are in flight together
+    uint32_t r[KB];
+#pragma unroll
+    for (int j = 0; j < KB; ++j) r[j] = (EXACT || j < nb) ? rr[kb + j] : 0u;
     u32x4 v[KB];
-    float wk[KB];
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
-      uint32_t r = 0;
-      float wj = 0.0f;
-      if (EXACT || j < nb) {
-        r = rr[kb + j];
-        wj = load_weight(weight, wd, t * K + kb + j);
-      }
-      if (r >= n_rows) {  // precondition violated: contribute nothing, stay in bounds
-        r = 0;
-        wj = 0.0f;
-      }
-      wk[j] = wj;
+      const uint32_t row = r[j] < n_rows ? r[j] : 0u;  // stay in bounds if violated
       v[j] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(down + static_cast<int64_t>(r) * H + h));
+          reinterpret_cast<const u32x4*>(down + static_cast<int64_t>(row) * H + h));
+    }
+    float wk[KB];
+    const int64_t w0 = t * K + kb;
+    if (wd == MOE_DTYPE_F32) {
+      const float* wf = static_cast<const float*>(weight) + w0;
+#pragma unroll
+      for (int j = 0; j < KB; ++j) wk[j] = (EXACT || j < nb) ? wf[j] : 0.0f;
+    } else {
+      const uint16_t* wh = static_cast<const uint16_t*>(weight) + w0;
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        const uint32_t b = (EXACT || j < nb) ? wh[j] : 0u;
+        wk[j] = wd == MOE_DTYPE_BF16 ? DBF16::widen_bits(b) : DF16::widen_bits(b);
+      }
     }
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
       if (!EXACT && j >= nb) break;
+      const float wj = r[j] < n_rows ? wk[j] : 0.0f;  // a violating row contributes nothing
       float d[VEC];
       widen16<DD>(v[j], d);
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[e] = fmaf(wk[j], d[e], acc[e]);
+      for (int e = 0; e < VEC; ++e) acc[e] = fmaf(wj, d[e], acc[e]);
     }
   }
   store_out<DO, VEC>(out + t * H + h, acc);

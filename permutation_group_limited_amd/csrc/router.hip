@@ -280,7 +280,7 @@ __global__ __launch_bounds__(kBlock) void router_kernel(
   }
   if (slot) {
     out_idx[t * K + sub] = static_cast<int32_t>(my_id);
-    out_w[t * K + sub] = static_cast<typename DS::storage>(DS::narrow_bits(w));
+    out_w[t * K + sub] = to_storage<DS>(w);
   }
 }
 
