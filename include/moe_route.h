@@ -106,6 +106,34 @@ moe_status_t moe_router_group_limited(int32_t* expert_indices, void* expert_weig
                                       float routed_scaling_factor, moe_group_score_t group_score,
                                       void* stream);
 
+/* Score functions the logits entry point applies before routing. */
+typedef enum {
+    MOE_SCORE_SIGMOID = 1, /* score = 1 / (1 + exp(-logit)) */
+    MOE_SCORE_SOFTMAX = 2  /* score = softmax of the token's E logits */
+} moe_score_fn_t;
+
+/*
+ * moe_router_group_limited_logits
+ * The router with the scores computed on the fly from logits: the page's
+ * optional scores_input_fn (Parameters: a loader of the score of a (token,
+ * expert) pair), here one of two fixed functions. Saves writing and reading
+ * a [T, E] scores tensor. Each score is evaluated in binary64 (softmax: max
+ * and sum over the token's experts) and rounded once to binary32; routing
+ * then proceeds exactly as in moe_router_group_limited, and expert_weights
+ * (dtype = logits_dtype) come from these scores.
+ *
+ *   router_logits    in [T, E], dtype logits_dtype.
+ *   other arguments, validation and support as moe_router_group_limited;
+ *   score_fn must be MOE_SCORE_SIGMOID or MOE_SCORE_SOFTMAX.
+ */
+moe_status_t moe_router_group_limited_logits(int32_t* expert_indices, void* expert_weights,
+                                             const void* router_logits, const void* expert_bias,
+                                             moe_dtype_t logits_dtype, moe_dtype_t bias_dtype,
+                                             moe_score_fn_t score_fn, int64_t T, int32_t E,
+                                             int32_t K, int32_t n_groups, int32_t topk_group,
+                                             int32_t norm_weights, float routed_scaling_factor,
+                                             moe_group_score_t group_score, void* stream);
+
 /*
  * moe_create_indices_workspace_size
  * Bytes of device workspace moe_create_indices needs for N slots and E

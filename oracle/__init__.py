@@ -32,6 +32,9 @@ BF16 = 1
 F16 = 2
 GROUP_TOP2_SUM = 0
 GROUP_MAX = 1
+SCORE_LOAD = 0
+SCORE_SIGMOID = 1
+SCORE_SOFTMAX = 2
 _ERRORS = {1: "invalid argument", 2: "input violates a precondition", 3: "out of memory"}
 
 _lib = None
@@ -67,7 +70,7 @@ def _load():
         p = ctypes.c_void_p
         i32, i64 = ctypes.c_int32, ctypes.c_int64
         lib.moe_oracle_router.argtypes = [p, p, p, p, i32, i32, i64, i32, i32, i32, i32, i32,
-                                          ctypes.c_float, i32]
+                                          ctypes.c_float, i32, i32]
         lib.moe_oracle_router.restype = ctypes.c_int
         lib.moe_oracle_create_indices.argtypes = [p, p, p, p, p, p, i64, i32]
         lib.moe_oracle_create_indices.restype = ctypes.c_int
@@ -110,9 +113,11 @@ def _encoded(a, dtype):
 
 def router(scores, bias, k: int, n_groups: int, topk_group: int, norm_weights: bool,
            routed_scaling_factor: float, group_score: int = GROUP_TOP2_SUM,
-           scores_dtype=None, bias_dtype=None):
+           scores_dtype=None, bias_dtype=None, score_fn: int = SCORE_LOAD):
     """Group-limited top-k router (group_limited_router_kernel page, description,
-    Parameters and Args). Returns (expert_indices int32 [T, K],
+    Parameters and Args). With score_fn SCORE_SIGMOID or SCORE_SOFTMAX the
+    `scores` argument holds logits and the scores are computed from them
+    (Parameters: scores_input_fn). Returns (expert_indices int32 [T, K],
     expert_weights [T, K] in the scores' dtype)."""
     s, sd = _encoded(scores, scores_dtype)
     b, bd = _encoded(bias, bias_dtype)
@@ -122,7 +127,7 @@ def router(scores, bias, k: int, n_groups: int, topk_group: int, norm_weights: b
     w = np.empty((T, k), dtype=np.float32 if sd == F32 else np.uint16)
     rc = _load().moe_oracle_router(_ptr(idx), _ptr(w), _ptr(s), _ptr(b), sd, bd, T, E, k,
                                    n_groups, topk_group, int(bool(norm_weights)),
-                                   ctypes.c_float(routed_scaling_factor), group_score)
+                                   ctypes.c_float(routed_scaling_factor), group_score, score_fn)
     _check(rc, "router")
     return idx, w
 

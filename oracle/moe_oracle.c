@@ -46,6 +46,7 @@
  * these numbers explicitly. */
 enum { OR_F32 = 0, OR_BF16 = 1, OR_F16 = 2 };
 enum { OR_GROUP_TOP2_SUM = 0, OR_GROUP_MAX = 1 };
+enum { OR_SCORE_LOAD = 0, OR_SCORE_SIGMOID = 1, OR_SCORE_SOFTMAX = 2 };
 enum { OR_OK = 0, OR_BAD_ARG = 1, OR_BAD_DATA = 2, OR_NO_MEM = 3 };
 
 int moe_oracle_num_threads(void) {
@@ -193,11 +194,38 @@ static int keyed_desc(const void* a, const void* b) {
  *     (Parameters: norm_weights; Args: routed_scaling_factor). This step is
  *     evaluated in binary64, rounded to binary32, then to the output dtype.
  */
+/*
+ * Routing scores of one token (router page, Parameters: scores_input_fn, an
+ * optional loader of the scores of a (token, expert) pair). score_fn 0
+ * loads them from the input; 1 and 2 compute them from the input taken as
+ * logits: 1 is the logistic sigmoid 1 / (1 + exp(-x)) of each logit, 2 the
+ * softmax over the token's E logits, exp(x_e - max) / sum_j exp(x_j - max).
+ * Both are evaluated in binary64 (sum in ascending expert order) and
+ * rounded once to binary32, the scores' working precision.
+ */
+static void token_scores(float* s, const void* in, int32_t dtype, int32_t score_fn, int64_t t,
+                         int32_t E) {
+    for (int32_t e = 0; e < E; ++e) s[e] = load_as_f32(in, dtype, t * (int64_t)E + e);
+    if (score_fn == OR_SCORE_SIGMOID) {
+        for (int32_t e = 0; e < E; ++e) s[e] = (float)(1.0 / (1.0 + exp(-(double)s[e])));
+    } else if (score_fn == OR_SCORE_SOFTMAX) {
+        double m = (double)s[0];
+        for (int32_t e = 1; e < E; ++e)
+            if ((double)s[e] > m) m = (double)s[e];
+        double sum = 0.0;
+        for (int32_t e = 0; e < E; ++e) sum += exp((double)s[e] - m);
+        for (int32_t e = 0; e < E; ++e) s[e] = (float)(exp((double)s[e] - m) / sum);
+    }
+}
+
 int moe_oracle_router(int32_t* expert_indices, void* expert_weights, const void* scores,
                       const void* bias, int32_t scores_dtype, int32_t bias_dtype, int64_t T,
                       int32_t E, int32_t K, int32_t n_groups, int32_t topk_group,
-                      int32_t norm_weights, float routed_scaling_factor, int32_t group_score) {
+                      int32_t norm_weights, float routed_scaling_factor, int32_t group_score,
+                      int32_t score_fn) {
     if (T < 0 || E <= 0 || n_groups <= 0 || E % n_groups != 0) return OR_BAD_ARG;
+    if (score_fn != OR_SCORE_LOAD && score_fn != OR_SCORE_SIGMOID && score_fn != OR_SCORE_SOFTMAX)
+        return OR_BAD_ARG;
     if (topk_group < 1 || topk_group > n_groups) return OR_BAD_ARG;
     const int32_t S = E / n_groups;
     if (K < 1 || K > topk_group * S) return OR_BAD_ARG;
@@ -219,11 +247,9 @@ int moe_oracle_router(int32_t* expert_indices, void* expert_weights, const void*
         } else {
 #pragma omp for schedule(static)
             for (int64_t t = 0; t < T; ++t) {
-                /* 1. biased scores */
-                for (int32_t e = 0; e < E; ++e) {
-                    s[e] = load_as_f32(scores, scores_dtype, t * (int64_t)E + e);
-                    b[e] = s[e] + load_as_f32(bias, bias_dtype, e);
-                }
+                /* 1. scores, biased scores */
+                token_scores(s, scores, scores_dtype, score_fn, t, E);
+                for (int32_t e = 0; e < E; ++e) b[e] = s[e] + load_as_f32(bias, bias_dtype, e);
                 /* 2. group scores */
                 for (int32_t g = 0; g < n_groups; ++g) {
                     for (int32_t j = 0; j < S; ++j) {

@@ -11,6 +11,8 @@ from .binding import (  # noqa: F401
     DTYPE_F32,
     GROUP_MAX,
     GROUP_TOP2_SUM,
+    SCORE_SIGMOID,
+    SCORE_SOFTMAX,
     MoeError,
     library_path,
     load_library,
@@ -18,4 +20,5 @@ from .binding import (  # noqa: F401
     moe_create_indices_workspace_size,
     moe_finalize,
     moe_router_group_limited,
+    moe_router_group_limited_logits,
 )

@@ -26,6 +26,8 @@ DTYPE_BF16 = 1
 DTYPE_F16 = 2
 GROUP_TOP2_SUM = 0
 GROUP_MAX = 1
+SCORE_SIGMOID = 1
+SCORE_SOFTMAX = 2
 
 _STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
            3: "MOE_ERR_ALIGNMENT", 4: "MOE_ERR_WORKSPACE", 5: "MOE_ERR_HIP"}
@@ -75,6 +77,9 @@ def load_library(check_runtime: bool = True):
     lib.moe_router_group_limited.argtypes = [p, p, p, p, i32, i32, i64, i32, i32, i32, i32, i32,
                                              ctypes.c_float, i32, p]
     lib.moe_router_group_limited.restype = ctypes.c_int
+    lib.moe_router_group_limited_logits.argtypes = [p, p, p, p, i32, i32, i32, i64, i32, i32,
+                                                    i32, i32, i32, ctypes.c_float, i32, p]
+    lib.moe_router_group_limited_logits.restype = ctypes.c_int
     lib.moe_create_indices_workspace_size.argtypes = [i64, i32]
     lib.moe_create_indices_workspace_size.restype = ctypes.c_size_t
     lib.moe_create_indices.argtypes = [p, p, p, p, p, p, i64, i32, p, ctypes.c_size_t, p, p]
@@ -155,6 +160,32 @@ def moe_router_group_limited(expert_indices: torch.Tensor, expert_weights: torch
         int(bool(norm_weights)), ctypes.c_float(routed_scaling_factor), int(group_score),
         _stream(stream, expert_scores))
     _check("moe_router_group_limited", st)
+
+
+def moe_router_group_limited_logits(expert_indices: torch.Tensor, expert_weights: torch.Tensor,
+                                    router_logits: torch.Tensor, expert_bias: torch.Tensor,
+                                    score_fn: int, n_groups: int, topk_group: int,
+                                    norm_weights: bool, routed_scaling_factor: float,
+                                    group_score: int = GROUP_TOP2_SUM, stream=None) -> None:
+    """As moe_router_group_limited, with the scores computed from router_logits
+    [T, E] by score_fn (SCORE_SIGMOID or SCORE_SOFTMAX); expert_weights take
+    the logits' dtype."""
+    lib = load_library()
+    _dev(expert_indices, expert_weights, router_logits, expert_bias)
+    T, E = router_logits.shape
+    K = expert_indices.shape[1]
+    if expert_indices.dtype != torch.int32 or tuple(expert_indices.shape) != (T, K):
+        raise ValueError("expert_indices must be int32 [T, K]")
+    if tuple(expert_weights.shape) != (T, K) or expert_weights.dtype != router_logits.dtype:
+        raise ValueError("expert_weights must be [T, K] with the logits' dtype")
+    if tuple(expert_bias.shape) != (E,):
+        raise ValueError("expert_bias must be [E]")
+    st = lib.moe_router_group_limited_logits(
+        _ptr(expert_indices), _ptr(expert_weights), _ptr(router_logits), _ptr(expert_bias),
+        _dtype_code(router_logits), _dtype_code(expert_bias), int(score_fn), T, E, K, n_groups,
+        topk_group, int(bool(norm_weights)), ctypes.c_float(routed_scaling_factor),
+        int(group_score), _stream(stream, router_logits))
+    _check("moe_router_group_limited_logits", st)
 
 
 def moe_create_indices_workspace_size(n: int, n_experts: int) -> int:

@@ -37,13 +37,13 @@ using namespace moe;
 
 extern "C" {
 
-moe_status_t moe_router_group_limited(int32_t* expert_indices, void* expert_weights,
-                                      const void* expert_scores, const void* expert_bias,
-                                      moe_dtype_t scores_dtype, moe_dtype_t bias_dtype,
-                                      int64_t T, int32_t E, int32_t K, int32_t n_groups,
-                                      int32_t topk_group, int32_t norm_weights,
-                                      float routed_scaling_factor, moe_group_score_t group_score,
-                                      void* stream) {
+static moe_status_t router_common(int32_t* expert_indices, void* expert_weights,
+                                  const void* expert_scores, const void* expert_bias,
+                                  moe_dtype_t scores_dtype, moe_dtype_t bias_dtype,
+                                  int32_t score_fn, int64_t T, int32_t E, int32_t K,
+                                  int32_t n_groups, int32_t topk_group, int32_t norm_weights,
+                                  float routed_scaling_factor, moe_group_score_t group_score,
+                                  void* stream) {
   if (T < 0 || E < 1 || n_groups < 1 || n_groups > 64 || E % n_groups != 0)
     return MOE_ERR_INVALID_ARG;
   if (topk_group < 1 || topk_group > n_groups) return MOE_ERR_INVALID_ARG;
@@ -62,9 +62,34 @@ moe_status_t moe_router_group_limited(int32_t* expert_indices, void* expert_weig
     return MOE_ERR_ALIGNMENT;
   if (T == 0) return MOE_OK;
   return launch_router(expert_indices, expert_weights, expert_scores, expert_bias, scores_dtype,
-                       bias_dtype, T, E, K, n_groups, topk_group, norm_weights ? 1 : 0,
+                       bias_dtype, score_fn, T, E, K, n_groups, topk_group, norm_weights ? 1 : 0,
                        routed_scaling_factor, static_cast<int32_t>(group_score),
                        static_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_router_group_limited(int32_t* expert_indices, void* expert_weights,
+                                      const void* expert_scores, const void* expert_bias,
+                                      moe_dtype_t scores_dtype, moe_dtype_t bias_dtype,
+                                      int64_t T, int32_t E, int32_t K, int32_t n_groups,
+                                      int32_t topk_group, int32_t norm_weights,
+                                      float routed_scaling_factor, moe_group_score_t group_score,
+                                      void* stream) {
+  return router_common(expert_indices, expert_weights, expert_scores, expert_bias, scores_dtype,
+                       bias_dtype, 0, T, E, K, n_groups, topk_group, norm_weights,
+                       routed_scaling_factor, group_score, stream);
+}
+
+moe_status_t moe_router_group_limited_logits(int32_t* expert_indices, void* expert_weights,
+                                             const void* router_logits, const void* expert_bias,
+                                             moe_dtype_t logits_dtype, moe_dtype_t bias_dtype,
+                                             moe_score_fn_t score_fn, int64_t T, int32_t E,
+                                             int32_t K, int32_t n_groups, int32_t topk_group,
+                                             int32_t norm_weights, float routed_scaling_factor,
+                                             moe_group_score_t group_score, void* stream) {
+  if (score_fn != MOE_SCORE_SIGMOID && score_fn != MOE_SCORE_SOFTMAX) return MOE_ERR_INVALID_ARG;
+  return router_common(expert_indices, expert_weights, router_logits, expert_bias, logits_dtype,
+                       bias_dtype, static_cast<int32_t>(score_fn), T, E, K, n_groups, topk_group,
+                       norm_weights, routed_scaling_factor, group_score, stream);
 }
 
 size_t moe_create_indices_workspace_size(int64_t N, int32_t E) {

@@ -111,10 +111,12 @@ __device__ __forceinline__ uint64_t match_any(uint32_t key, int nbits, uint64_t 
 
 // ---- launchers (host side), one per stage --------------------------------
 
+// score_fn: 0 = scores given, 1 = sigmoid of logits, 2 = softmax of logits
 moe_status_t launch_router(int32_t* expert_indices, void* expert_weights, const void* scores,
                            const void* bias, moe_dtype_t scores_dtype, moe_dtype_t bias_dtype,
-                           int64_t T, int32_t E, int32_t K, int32_t n_groups, int32_t topk_group,
-                           int32_t norm_weights, float scale, int32_t mode, hipStream_t stream);
+                           int32_t score_fn, int64_t T, int32_t E, int32_t K, int32_t n_groups,
+                           int32_t topk_group, int32_t norm_weights, float scale, int32_t mode,
+                           hipStream_t stream);
 
 struct IndexPlan {
   int waves;        // waves per workgroup (16 when E <= 256, else 4)

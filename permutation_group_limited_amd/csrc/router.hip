@@ -164,7 +164,30 @@ __device__ __forceinline__ void sort_desc(uint32_t (&k)[EPL], uint32_t (&e)[EPL]
   }
 }
 
-template <typename DS, typename DB, int EPL, int LPT>
+// Score functions applied to logits before routing (the page's optional
+// scores_input_fn): evaluated in binary64, rounded once to binary32.
+constexpr int kScoreLoad = 0;
+constexpr int kScoreSigmoid = 1;
+constexpr int kScoreSoftmax = 2;
+
+__device__ __forceinline__ float sigmoid_f64(float x) {
+  return static_cast<float>(1.0 / (1.0 + exp(-static_cast<double>(x))));
+}
+
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+
+// Sum of v over the token's LPT lanes (xor butterfly; every lane of the
+// segment ends with the same value because each pairwise add is commutative).
+template <int LPT>
+__device__ __forceinline__ double segment_sum_f64(double v) {
+#pragma unroll
+  for (int off = 1; off < LPT; off <<= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+template <typename DS, typename DB, int EPL, int LPT, int FN>
 __global__ __launch_bounds__(kBlock) void router_kernel(
     int32_t* __restrict__ out_idx, typename DS::storage* __restrict__ out_w,
     const typename DS::storage* __restrict__ scores, const typename DB::storage* __restrict__ bias,
@@ -191,6 +214,26 @@ __global__ __launch_bounds__(kBlock) void router_kernel(
     for (int i = 0; i < EPL; ++i) s[i] = 0.0f;
   }
   load_row<DB, EPL>(bi, bias + e0);
+  // scores from logits (FN != kScoreLoad)
+  double sm_max = 0.0, sm_sum = 1.0;
+  if constexpr (FN == kScoreSigmoid) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) s[i] = sigmoid_f64(s[i]);
+  } else if constexpr (FN == kScoreSoftmax) {
+    uint32_t km = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) km = umax(km, ordered_key(s[i]));
+    sm_max = static_cast<double>(key_to_float(segment_max<LPT>(km)));
+    double ex[EPL], part = 0.0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      ex[i] = exp(static_cast<double>(s[i]) - sm_max);
+      part += ex[i];
+    }
+    sm_sum = segment_sum_f64<LPT>(part);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) s[i] = static_cast<float>(ex[i] / sm_sum);
+  }
 #pragma unroll
   for (int i = 0; i < EPL; ++i) b[i] = s[i] + bi[i];
 
@@ -264,7 +307,13 @@ __global__ __launch_bounds__(kBlock) void router_kernel(
   // ---- weights from the unbiased scores -----------------------------------
   const bool slot = tok_ok && sub < K;
   if (my_id >= static_cast<uint32_t>(E)) my_id = 0;  // unreachable with finite scores
-  const float u = slot ? load_f32<DS>(scores, t * E + my_id) : 0.0f;
+  float u = 0.0f;
+  if (slot) {
+    u = load_f32<DS>(scores, t * E + my_id);
+    if constexpr (FN == kScoreSigmoid) u = sigmoid_f64(u);
+    if constexpr (FN == kScoreSoftmax)
+      u = static_cast<float>(exp(static_cast<double>(u) - sm_max) / sm_sum);
+  }
   float w;
   if (norm_weights) {
     float d = 0.0f;
@@ -284,25 +333,26 @@ __global__ __launch_bounds__(kBlock) void router_kernel(
   }
 }
 
-template <typename DS, typename DB, int EPL, int LPT>
+template <typename DS, typename DB, int EPL, int LPT, int FN>
 moe_status_t launch_router_t(int32_t* idx, void* w, const void* s, const void* b, int64_t T,
                              int32_t K, int32_t G, int32_t TG, int32_t norm, float scale,
                              int32_t mode, hipStream_t stream) {
   constexpr int TPB = kWavesPerBlock * (kWave / LPT);  // tokens per block
   const int64_t blocks = (T + TPB - 1) / TPB;
-  hipLaunchKernelGGL((router_kernel<DS, DB, EPL, LPT>), dim3(static_cast<uint32_t>(blocks)),
+  hipLaunchKernelGGL((router_kernel<DS, DB, EPL, LPT, FN>), dim3(static_cast<uint32_t>(blocks)),
                      dim3(kBlock), 0, stream, idx, static_cast<typename DS::storage*>(w),
                      static_cast<const typename DS::storage*>(s),
                      static_cast<const typename DB::storage*>(b), T, K, G, TG, norm, scale, mode);
   return check_launch();
 }
 
-template <typename DS, typename DB>
+template <typename DS, typename DB, int FN>
 moe_status_t launch_router_e(int32_t* idx, void* w, const void* s, const void* b, int64_t T,
                              int32_t E, int32_t K, int32_t G, int32_t TG, int32_t norm,
                              float scale, int32_t mode, hipStream_t stream) {
-#define MOE_R(EPL, LPT) \
-  return launch_router_t<DS, DB, EPL, LPT>(idx, w, s, b, T, K, G, TG, norm, scale, mode, stream)
+#define MOE_R(EPL, LPT)                                                                     \
+  return launch_router_t<DS, DB, EPL, LPT, FN>(idx, w, s, b, T, K, G, TG, norm, scale, mode, \
+                                               stream)
   switch (E) {
     case 1: MOE_R(1, 1);
     case 2: MOE_R(1, 2);
@@ -320,22 +370,39 @@ moe_status_t launch_router_e(int32_t* idx, void* w, const void* s, const void* b
 #undef MOE_R
 }
 
+template <typename DS, typename DB>
+moe_status_t launch_router_fn(int32_t* idx, void* w, const void* s, const void* b, int64_t T,
+                              int32_t E, int32_t K, int32_t G, int32_t TG, int32_t norm,
+                              float scale, int32_t mode, int32_t fn, hipStream_t stream) {
+  switch (fn) {
+    case kScoreLoad:
+      return launch_router_e<DS, DB, kScoreLoad>(idx, w, s, b, T, E, K, G, TG, norm, scale,
+                                                 mode, stream);
+    case kScoreSigmoid:
+      return launch_router_e<DS, DB, kScoreSigmoid>(idx, w, s, b, T, E, K, G, TG, norm, scale,
+                                                    mode, stream);
+    case kScoreSoftmax:
+      return launch_router_e<DS, DB, kScoreSoftmax>(idx, w, s, b, T, E, K, G, TG, norm, scale,
+                                                    mode, stream);
+    default:
+      return MOE_ERR_INVALID_ARG;
+  }
+}
+
 }  // namespace
 
 moe_status_t launch_router(int32_t* idx, void* w, const void* s, const void* b,
-                           moe_dtype_t sd, moe_dtype_t bd, int64_t T, int32_t E, int32_t K,
-                           int32_t G, int32_t TG, int32_t norm, float scale, int32_t mode,
-                           hipStream_t stream) {
-  if (sd == MOE_DTYPE_F32 && bd == MOE_DTYPE_F32)
-    return launch_router_e<DF32, DF32>(idx, w, s, b, T, E, K, G, TG, norm, scale, mode, stream);
-  if (sd == MOE_DTYPE_BF16 && bd == MOE_DTYPE_BF16)
-    return launch_router_e<DBF16, DBF16>(idx, w, s, b, T, E, K, G, TG, norm, scale, mode, stream);
-  if (sd == MOE_DTYPE_BF16 && bd == MOE_DTYPE_F32)
-    return launch_router_e<DBF16, DF32>(idx, w, s, b, T, E, K, G, TG, norm, scale, mode, stream);
-  if (sd == MOE_DTYPE_F16 && bd == MOE_DTYPE_F16)
-    return launch_router_e<DF16, DF16>(idx, w, s, b, T, E, K, G, TG, norm, scale, mode, stream);
-  if (sd == MOE_DTYPE_F16 && bd == MOE_DTYPE_F32)
-    return launch_router_e<DF16, DF32>(idx, w, s, b, T, E, K, G, TG, norm, scale, mode, stream);
+                           moe_dtype_t sd, moe_dtype_t bd, int32_t fn, int64_t T, int32_t E,
+                           int32_t K, int32_t G, int32_t TG, int32_t norm, float scale,
+                           int32_t mode, hipStream_t stream) {
+#define MOE_D(DS, DB) \
+  return launch_router_fn<DS, DB>(idx, w, s, b, T, E, K, G, TG, norm, scale, mode, fn, stream)
+  if (sd == MOE_DTYPE_F32 && bd == MOE_DTYPE_F32) MOE_D(DF32, DF32);
+  if (sd == MOE_DTYPE_BF16 && bd == MOE_DTYPE_BF16) MOE_D(DBF16, DBF16);
+  if (sd == MOE_DTYPE_BF16 && bd == MOE_DTYPE_F32) MOE_D(DBF16, DF32);
+  if (sd == MOE_DTYPE_F16 && bd == MOE_DTYPE_F16) MOE_D(DF16, DF16);
+  if (sd == MOE_DTYPE_F16 && bd == MOE_DTYPE_F32) MOE_D(DF16, DF32);
+#undef MOE_D
   return MOE_ERR_UNSUPPORTED;
 }
 

@@ -77,13 +77,19 @@ WORKLOADS = {
 }
 
 
-def make_scores(w: Workload) -> torch.Tensor:
-    """Routing scores [T, E] fp32 on the CPU."""
+def make_logits(w: Workload) -> torch.Tensor:
+    """Router logits [T, E] fp32 on the CPU (the scores are a function of them)."""
     g = torch.Generator().manual_seed(w.seed)
     logits = torch.randn(w.T, w.E, generator=g, dtype=torch.float32)
     if w.skew:
         rank = torch.arange(1, w.E + 1, dtype=torch.float64)
         logits = logits + (3.0 * rank.pow(-1.2)).to(torch.float32)
+    return logits.contiguous()
+
+
+def make_scores(w: Workload) -> torch.Tensor:
+    """Routing scores [T, E] fp32 on the CPU."""
+    logits = make_logits(w)
     if w.score_fn == "softmax":
         return torch.softmax(logits, dim=-1).contiguous()
     return torch.sigmoid(logits).contiguous()

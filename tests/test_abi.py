@@ -125,3 +125,15 @@ def test_binding_rejects_host_tensors(lib):
     with pytest.raises(ValueError):
         binding.moe_finalize(x, torch.zeros(8, 8), torch.zeros(8, dtype=torch.int32),
                              torch.zeros(4, 2))
+
+
+@pytest.mark.parametrize("fn,code", [(0, INVALID), (3, INVALID)])
+def test_logits_router_rejects_bad_score_fn(lib, fn, code):
+    assert lib.moe_router_group_limited_logits(FAKE, FAKE, FAKE, FAKE, 0, 0, fn, 4, 256, 8, 8, 4,
+                                               1, ctypes.c_float(1.0), 0, None) == code
+
+
+def test_logits_router_validates_like_router(lib):
+    # same shape checks as the plain router (E % n_groups != 0)
+    assert lib.moe_router_group_limited_logits(FAKE, FAKE, FAKE, FAKE, 0, 0, 1, 4, 256, 8, 3, 1,
+                                               1, ctypes.c_float(1.0), 0, None) == INVALID

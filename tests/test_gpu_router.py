@@ -6,6 +6,7 @@ import pytest
 import torch
 
 import oracle
+from permutation_group_limited_amd import binding
 from permutation_group_limited_amd import workloads as wl
 
 from _gpu import (assert_16bit_within_one_ulp, assert_weights_close, bf16_bits, encode,
@@ -108,3 +109,56 @@ def test_16bit_scores(sd, bd, T, E, G, TG, K):
                                bias_dtype=None if bd == "f32" else bcode)
         assert np.array_equal(gi, oi)
         assert_16bit_within_one_ulp(bf16_bits(gw), ow, "router weights")
+
+
+def gpu_router_logits(logits, bias, fn, K, G, TG, norm, scale, mode=0):
+    T, E = logits.shape
+    x = logits.to("cuda:0")
+    b = bias.to("cuda:0")
+    idx = torch.full((T, K), -7, dtype=torch.int32, device="cuda:0")
+    w = torch.full((T, K), float("nan"), dtype=logits.dtype, device="cuda:0")
+    binding.moe_router_group_limited_logits(idx, w, x, b, fn, G, TG, norm, scale, mode)
+    torch.cuda.synchronize()
+    wh = w.cpu()
+    return idx.cpu().numpy(), (wh.numpy() if wh.dtype == torch.float32 else wh)
+
+
+FNS = {"sigmoid": (binding.SCORE_SIGMOID, oracle.SCORE_SIGMOID),
+       "softmax": (binding.SCORE_SOFTMAX, oracle.SCORE_SOFTMAX)}
+
+
+@pytest.mark.parametrize("name", ["tiny", "mixtral", "dsv3", "decode", "skewed"])
+def test_logits_workload_full_size(name):
+    w = wl.WORKLOADS[name]
+    log("router logits workload", w.describe(), w.score_fn)
+    x, b = wl.make_logits(w), wl.make_bias(w)
+    gfn, ofn = FNS[w.score_fn]
+    gi, gw = gpu_router_logits(x, b, gfn, w.K, w.n_groups, w.topk_group, w.norm_weights,
+                               w.scale)
+    oi, ow = oracle.router(x.numpy(), b.numpy(), w.K, w.n_groups, w.topk_group,
+                           w.norm_weights, w.scale, score_fn=ofn)
+    assert np.array_equal(gi, oi), "indices differ in %d tokens" % np.sum(np.any(gi != oi, 1))
+    assert_weights_close(gw, ow)
+
+
+@pytest.mark.parametrize("fn", ["sigmoid", "softmax"])
+@pytest.mark.parametrize("T,E,G,TG,K", [(33, 8, 4, 2, 3), (129, 32, 8, 4, 6), (300, 128, 8, 4, 8),
+                                        (511, 256, 8, 4, 8), (61, 1024, 64, 8, 16),
+                                        (77, 64, 1, 1, 6)])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_logits_random_shapes(fn, T, E, G, TG, K, dt):
+    log("router logits", fn, T, E, G, TG, K, dt)
+    g = torch.Generator().manual_seed(T * E + K)
+    x = (torch.randn(T, E, generator=g) * 3).to(DTYPES[dt])
+    b = (torch.randn(E, generator=g) * 0.02)
+    gfn, ofn = FNS[fn]
+    for norm in (True, False):
+        gi, gw = gpu_router_logits(x, b, gfn, K, G, TG, norm, 1.5)
+        xn, xcode = encode(x)
+        oi, ow = oracle.router(xn, b.numpy(), K, G, TG, norm, 1.5, scores_dtype=xcode,
+                               score_fn=ofn)
+        assert np.array_equal(gi, oi)
+        if dt == "f32":
+            assert_weights_close(gw, ow)
+        else:
+            assert_16bit_within_one_ulp(bf16_bits(gw), ow, "router weights")
