@@ -164,8 +164,9 @@ size_t moe_create_indices_workspace_size(int64_t N, int32_t E);
  *                         moe_create_indices_workspace_size(N, E) bytes
  *                         (may be NULL when that size is 0). Contents on
  *                         entry do not matter; clobbered on exit.
- *   scales_offset_p       must be NULL (aligned scale offsets for block-scaled
- *                         grouped matmul are not produced by this build).
+ *   scales_offset_p       must be NULL here (no alignment is known to this
+ *                         call); moe_create_indices_aligned produces the
+ *                         aligned scale offsets.
  *
  * Precondition: 0 <= topk_ids[i] < E. A slot whose id is out of range is left
  * out of every count, its restore entry is set to 0xFFFFFFFF and the
@@ -178,6 +179,31 @@ moe_status_t moe_create_indices(uint32_t* token_expert_order, uint32_t* expert_s
                                 uint32_t* expert_usage_stats, const int32_t* topk_ids,
                                 int64_t N, int32_t E, void* workspace, size_t workspace_bytes,
                                 uint32_t* scales_offset_p, void* stream);
+
+/*
+ * moe_create_indices_aligned
+ * moe_create_indices plus the page's optional output scales_offset_p
+ * ("aligned scale offsets for FP8/block-scaled grouped matmul"), padded as
+ * the TokenFormat page's pad_expert_offsets pads offsets to the grouped
+ * matmul's alignment. The pages name no alignment, so it is an argument.
+ *
+ *   scales_offset   out uint32 [E + 1], required: entry j = start of active
+ *                   expert j's block of scale rows when every active expert's
+ *                   row count is rounded up to a multiple of scale_align
+ *                   (experts in expert_ids order); entry A (A = active
+ *                   experts) is the padded total, entries after A repeat it.
+ *   scale_align     rows per scale block, >= 1; N + E * (scale_align - 1)
+ *                   must stay below 2^32. With scale_align = 1 the offsets
+ *                   equal expert_start_indices.
+ *   all other arguments and outputs as moe_create_indices.
+ */
+moe_status_t moe_create_indices_aligned(uint32_t* token_expert_order,
+                                        uint32_t* expert_start_indices,
+                                        uint32_t* restore_token_order, int32_t* expert_ids,
+                                        uint32_t* expert_usage_stats, const int32_t* topk_ids,
+                                        int64_t N, int32_t E, void* workspace,
+                                        size_t workspace_bytes, uint32_t* scales_offset,
+                                        uint32_t scale_align, void* stream);
 
 /*
  * moe_finalize

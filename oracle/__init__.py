@@ -74,6 +74,8 @@ def _load():
         lib.moe_oracle_router.restype = ctypes.c_int
         lib.moe_oracle_create_indices.argtypes = [p, p, p, p, p, p, i64, i32]
         lib.moe_oracle_create_indices.restype = ctypes.c_int
+        lib.moe_oracle_scale_offsets.argtypes = [p, p, i64, i32, ctypes.c_uint32]
+        lib.moe_oracle_scale_offsets.restype = ctypes.c_int
         lib.moe_oracle_finalize.argtypes = [p, i32, p, i32, p, p, i32, i64, i32, i64]
         lib.moe_oracle_finalize.restype = ctypes.c_int
         for fn in ("moe_oracle_f32_to_bf16_array", "moe_oracle_f32_to_f16_array",
@@ -150,6 +152,18 @@ def create_indices(topk_ids, n_experts: int):
         _ptr(out["restore_token_order"]), _ptr(out["expert_ids"]),
         _ptr(out["expert_usage_stats"]), _ptr(ids), n, n_experts)
     _check(rc, "create_indices")
+    return out
+
+
+def scale_offsets(topk_ids, n_experts: int, align: int) -> np.ndarray:
+    """Aligned scale offsets [E + 1] uint32 (moe_create_indices page, Args:
+    scales_offset_p; TokenFormat page, pad_expert_offsets): start of each
+    active expert's scale rows when every active expert's row count is
+    rounded up to a multiple of `align`."""
+    ids = np.ascontiguousarray(topk_ids, dtype=np.int32).reshape(-1)
+    out = np.empty(n_experts + 1, dtype=np.uint32)
+    rc = _load().moe_oracle_scale_offsets(_ptr(out), _ptr(ids), ids.shape[0], n_experts, align)
+    _check(rc, "scale_offsets")
     return out
 
 

@@ -374,6 +374,38 @@ int moe_oracle_create_indices(uint32_t* token_expert_order, uint32_t* expert_sta
     return OR_OK;
 }
 
+/*
+ * Aligned scale offsets for a block-scaled grouped matmul (moe_create_indices
+ * page, Args: scales_offset_p "aligned scale offsets"; TokenFormat page,
+ * pad_expert_offsets: offsets padded to the grouped matmul's alignment).
+ * The pages give no alignment, so it is an argument. By reading, entry j of
+ * scales_offset [E + 1] is where active expert j's block of scale rows
+ * starts when every active expert's row count is rounded up to a multiple
+ * of `align`; entry A (A = active experts) is the padded total and the
+ * entries after A repeat it. Experts are in the expert_ids order
+ * (ascending id).
+ */
+int moe_oracle_scale_offsets(uint32_t* scales_offset, const int32_t* topk_ids, int64_t N,
+                             int32_t E, uint32_t align) {
+    if (N < 0 || N > (int64_t)UINT32_MAX || E <= 0 || align == 0) return OR_BAD_ARG;
+    for (int64_t i = 0; i < N; ++i)
+        if (topk_ids[i] < 0 || topk_ids[i] >= E) return OR_BAD_DATA;
+    uint64_t* count = (uint64_t*)calloc((size_t)E, sizeof(uint64_t));
+    if (!count) return OR_NO_MEM;
+    for (int64_t i = 0; i < N; ++i) count[topk_ids[i]] += 1;
+    uint64_t offset = 0;
+    uint32_t j = 0;
+    for (int32_t e = 0; e < E; ++e) {
+        if (count[e] == 0) continue;
+        scales_offset[j++] = (uint32_t)offset;
+        offset += (count[e] + align - 1) / align * align;
+    }
+    free(count);
+    if (offset > UINT32_MAX) return OR_BAD_ARG;
+    for (; j <= (uint32_t)E; ++j) scales_offset[j] = (uint32_t)offset;
+    return OR_OK;
+}
+
 /* ------------------------------------------------------------------ */
 /* Finalize (moe_finalize page)                                        */
 /* ------------------------------------------------------------------ */

@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     library_path,
     load_library,
     moe_create_indices,
+    moe_create_indices_aligned,
     moe_create_indices_workspace_size,
     moe_finalize,
     moe_router_group_limited,

@@ -84,6 +84,9 @@ def load_library(check_runtime: bool = True):
     lib.moe_create_indices_workspace_size.restype = ctypes.c_size_t
     lib.moe_create_indices.argtypes = [p, p, p, p, p, p, i64, i32, p, ctypes.c_size_t, p, p]
     lib.moe_create_indices.restype = ctypes.c_int
+    lib.moe_create_indices_aligned.argtypes = [p, p, p, p, p, p, i64, i32, p, ctypes.c_size_t, p,
+                                               ctypes.c_uint32, p]
+    lib.moe_create_indices_aligned.restype = ctypes.c_int
     lib.moe_finalize.argtypes = [p, i32, p, i32, p, p, i32, i64, i32, i64, p]
     lib.moe_finalize.restype = ctypes.c_int
     lib.moe_status_string.argtypes = [i32]
@@ -223,6 +226,39 @@ def moe_create_indices(token_expert_order: torch.Tensor, expert_start_indices: t
         _ptr(expert_ids), _ptr(expert_usage_stats), _ptr(topk_ids), n, E, _ptr(workspace),
         ws_bytes, scales_offset_p, _stream(stream, topk_ids, expert_ids))
     _check("moe_create_indices", st)
+
+
+def moe_create_indices_aligned(token_expert_order: torch.Tensor,
+                               expert_start_indices: torch.Tensor,
+                               restore_token_order: torch.Tensor, expert_ids: torch.Tensor,
+                               expert_usage_stats: torch.Tensor, topk_ids: torch.Tensor,
+                               workspace: torch.Tensor, scales_offset: torch.Tensor,
+                               scale_align: int, stream=None) -> None:
+    """moe_create_indices plus scales_offset [E+1]: per active expert, the start
+    of its scale rows with every expert's row count rounded up to scale_align."""
+    lib = load_library()
+    _dev(token_expert_order, expert_start_indices, restore_token_order, expert_ids,
+         expert_usage_stats, topk_ids, workspace, scales_offset)
+    for t, name in ((token_expert_order, "token_expert_order"),
+                    (expert_start_indices, "expert_start_indices"),
+                    (restore_token_order, "restore_token_order"), (expert_ids, "expert_ids"),
+                    (expert_usage_stats, "expert_usage_stats"), (topk_ids, "topk_ids"),
+                    (scales_offset, "scales_offset")):
+        _int32_like(t, name)
+    n = topk_ids.numel()
+    E = expert_ids.numel()
+    if token_expert_order.numel() != n or restore_token_order.numel() != n:
+        raise ValueError("token_expert_order and restore_token_order need N entries")
+    if expert_start_indices.numel() != E + 1 or expert_usage_stats.numel() != 2 or \
+            scales_offset.numel() != E + 1:
+        raise ValueError("expert_start_indices and scales_offset need E+1 entries, "
+                         "expert_usage_stats 2")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.moe_create_indices_aligned(
+        _ptr(token_expert_order), _ptr(expert_start_indices), _ptr(restore_token_order),
+        _ptr(expert_ids), _ptr(expert_usage_stats), _ptr(topk_ids), n, E, _ptr(workspace),
+        ws_bytes, _ptr(scales_offset), int(scale_align), _stream(stream, topk_ids, expert_ids))
+    _check("moe_create_indices_aligned", st)
 
 
 def moe_finalize(output: torch.Tensor, down: torch.Tensor, restore_order: torch.Tensor,

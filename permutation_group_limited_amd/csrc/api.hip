@@ -97,26 +97,54 @@ size_t moe_create_indices_workspace_size(int64_t N, int32_t E) {
   return plan_indices(N, E).workspace_bytes;
 }
 
-moe_status_t moe_create_indices(uint32_t* token_expert_order, uint32_t* expert_start_indices,
-                                uint32_t* restore_token_order, int32_t* expert_ids,
-                                uint32_t* expert_usage_stats, const int32_t* topk_ids,
-                                int64_t N, int32_t E, void* workspace, size_t workspace_bytes,
-                                uint32_t* scales_offset_p, void* stream) {
+static moe_status_t indices_common(uint32_t* token_expert_order,
+                                   uint32_t* expert_start_indices, uint32_t* restore_token_order,
+                                   int32_t* expert_ids, uint32_t* expert_usage_stats,
+                                   const int32_t* topk_ids, int64_t N, int32_t E,
+                                   void* workspace, size_t workspace_bytes,
+                                   uint32_t* scales_offset, uint32_t scale_align, void* stream) {
   if (N < 0 || N > (int64_t)UINT32_MAX || E < 1 || E > 1024) return MOE_ERR_INVALID_ARG;
   if (!expert_start_indices || !expert_ids || !expert_usage_stats) return MOE_ERR_INVALID_ARG;
   if (N > 0 && (!token_expert_order || !restore_token_order || !topk_ids))
     return MOE_ERR_INVALID_ARG;
-  if (scales_offset_p != nullptr) return MOE_ERR_UNSUPPORTED;
+  if (scales_offset != nullptr &&
+      (scale_align == 0 || N + static_cast<int64_t>(E) * (scale_align - 1) > (int64_t)UINT32_MAX))
+    return MOE_ERR_INVALID_ARG;
   const IndexPlan plan = plan_indices(N, E);
   if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
     return MOE_ERR_WORKSPACE;
   if (!aligned(workspace, 4) || !aligned(token_expert_order, 4) ||
       !aligned(expert_start_indices, 4) || !aligned(restore_token_order, 4) ||
-      !aligned(expert_ids, 4) || !aligned(expert_usage_stats, 4) || !aligned(topk_ids, 4))
+      !aligned(expert_ids, 4) || !aligned(expert_usage_stats, 4) || !aligned(topk_ids, 4) ||
+      !aligned(scales_offset, 4))
     return MOE_ERR_ALIGNMENT;
   return launch_indices(token_expert_order, expert_start_indices, restore_token_order, expert_ids,
-                        expert_usage_stats, topk_ids, N, E, workspace, plan,
-                        static_cast<hipStream_t>(stream));
+                        expert_usage_stats, scales_offset, scale_align, topk_ids, N, E,
+                        workspace, plan, static_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_create_indices(uint32_t* token_expert_order, uint32_t* expert_start_indices,
+                                uint32_t* restore_token_order, int32_t* expert_ids,
+                                uint32_t* expert_usage_stats, const int32_t* topk_ids,
+                                int64_t N, int32_t E, void* workspace, size_t workspace_bytes,
+                                uint32_t* scales_offset_p, void* stream) {
+  if (scales_offset_p != nullptr) return MOE_ERR_UNSUPPORTED;
+  return indices_common(token_expert_order, expert_start_indices, restore_token_order,
+                        expert_ids, expert_usage_stats, topk_ids, N, E, workspace,
+                        workspace_bytes, nullptr, 0, stream);
+}
+
+moe_status_t moe_create_indices_aligned(uint32_t* token_expert_order,
+                                        uint32_t* expert_start_indices,
+                                        uint32_t* restore_token_order, int32_t* expert_ids,
+                                        uint32_t* expert_usage_stats, const int32_t* topk_ids,
+                                        int64_t N, int32_t E, void* workspace,
+                                        size_t workspace_bytes, uint32_t* scales_offset,
+                                        uint32_t scale_align, void* stream) {
+  if (scales_offset == nullptr) return MOE_ERR_INVALID_ARG;
+  return indices_common(token_expert_order, expert_start_indices, restore_token_order,
+                        expert_ids, expert_usage_stats, topk_ids, N, E, workspace,
+                        workspace_bytes, scales_offset, scale_align, stream);
 }
 
 moe_status_t moe_finalize(void* output, moe_dtype_t out_dtype, const void* down,

@@ -127,10 +127,12 @@ struct IndexPlan {
 };
 IndexPlan plan_indices(int64_t N, int32_t E);
 
+// scales_offset may be NULL (then scale_align is ignored)
 moe_status_t launch_indices(uint32_t* token_expert_order, uint32_t* expert_start_indices,
                             uint32_t* restore_token_order, int32_t* expert_ids,
-                            uint32_t* expert_usage_stats, const int32_t* topk_ids, int64_t N,
-                            int32_t E, void* workspace, const IndexPlan& plan, hipStream_t stream);
+                            uint32_t* expert_usage_stats, uint32_t* scales_offset,
+                            uint32_t scale_align, const int32_t* topk_ids, int64_t N, int32_t E,
+                            void* workspace, const IndexPlan& plan, hipStream_t stream);
 
 moe_status_t launch_finalize(void* output, moe_dtype_t out_dtype, const void* down,
                              moe_dtype_t down_dtype, const uint32_t* restore_order,

@@ -19,7 +19,8 @@
 //      every slot at  start(expert) + slots of that expert in earlier chunks
 //      + in earlier waves + in earlier lanes of this 64-slot round, the last
 //      term from a ballot-built peer mask and mbcnt. Workgroup 0 also writes
-//      expert_ids, expert_start_indices and the stats.
+//      expert_ids, expert_start_indices and the stats (and, when asked, the
+//      aligned scale offsets).
 // A problem that fits one chunk skips step 1 (one launch in total).
 //
 // Both kernels are latency-bound (N * 12 bytes in all), so every wave issues
@@ -140,6 +141,7 @@ template <int W>
 __global__ __launch_bounds__(W * kWave) void index_scatter_kernel(
     uint32_t* __restrict__ order, uint32_t* __restrict__ starts, uint32_t* __restrict__ restore,
     int32_t* __restrict__ expert_ids, uint32_t* __restrict__ stats,
+    uint32_t* __restrict__ scales_offset, uint32_t scale_align,
     const int32_t* __restrict__ ids, const uint32_t* __restrict__ counts, int64_t N, int32_t E,
     int64_t chunk, int64_t nchunks, int rounds) {
   constexpr int kThreads = W * kWave;
@@ -321,6 +323,30 @@ __global__ __launch_bounds__(W * kWave) void index_scatter_kernel(
       stats[0] = most;
       stats[1] = n_active;
     }
+    if (scales_offset != nullptr) {  // uniform
+      // every active expert's rows rounded up to a multiple of scale_align
+      uint32_t local_pad = 0;
+#pragma unroll
+      for (int j = 0; j < kMaxEPT; ++j) {
+        const uint32_t c = tot[j];
+        local_pad += (c + scale_align - 1u) / scale_align * scale_align;
+      }
+      uint32_t pad_total = 0;
+      uint32_t pad = block_exclusive_scan<W>(local_pad, tmp, &pad_total);
+      uint32_t s2 = block_exclusive_scan<W>(local_active, tmp, &n_active);
+#pragma unroll
+      for (int j = 0; j < kMaxEPT; ++j) {
+        const int e = static_cast<int>(threadIdx.x) * EPT + j;
+        if (j < EPT && e < E && tot[j] != 0u) {
+          scales_offset[s2] = pad;
+          ++s2;
+        }
+        pad += (tot[j] + scale_align - 1u) / scale_align * scale_align;
+      }
+      for (int x = static_cast<int>(n_active) + static_cast<int>(threadIdx.x); x <= E;
+           x += kThreads)
+        scales_offset[x] = pad_total;
+    }
   }
   __syncthreads();
 
@@ -382,9 +408,9 @@ IndexPlan plan_indices(int64_t N, int32_t E) {
 namespace {
 template <int W>
 moe_status_t launch_indices_t(uint32_t* order, uint32_t* starts, uint32_t* restore,
-                              int32_t* expert_ids, uint32_t* stats, const int32_t* ids, int64_t N,
-                              int32_t E, uint32_t* counts, const IndexPlan& plan,
-                              hipStream_t stream) {
+                              int32_t* expert_ids, uint32_t* stats, uint32_t* scales,
+                              uint32_t align, const int32_t* ids, int64_t N, int32_t E,
+                              uint32_t* counts, const IndexPlan& plan, hipStream_t stream) {
   if (plan.nchunks > 1) {
     hipLaunchKernelGGL(index_hist_kernel<W>, dim3(static_cast<uint32_t>(plan.nchunks)),
                        dim3(W * kWave), 0, stream, counts, ids, N, E, plan.chunk, plan.rounds);
@@ -392,23 +418,23 @@ moe_status_t launch_indices_t(uint32_t* order, uint32_t* starts, uint32_t* resto
     if (st != MOE_OK) return st;
   }
   hipLaunchKernelGGL(index_scatter_kernel<W>, dim3(static_cast<uint32_t>(plan.nchunks)),
-                     dim3(W * kWave), 0, stream, order, starts, restore, expert_ids, stats, ids,
-                     static_cast<const uint32_t*>(counts), N, E, plan.chunk, plan.nchunks,
-                     plan.rounds);
+                     dim3(W * kWave), 0, stream, order, starts, restore, expert_ids, stats, scales,
+                     align, ids, static_cast<const uint32_t*>(counts), N, E, plan.chunk,
+                     plan.nchunks, plan.rounds);
   return check_launch();
 }
 }  // namespace
 
 moe_status_t launch_indices(uint32_t* order, uint32_t* starts, uint32_t* restore,
-                            int32_t* expert_ids, uint32_t* stats, const int32_t* ids, int64_t N,
-                            int32_t E, void* workspace, const IndexPlan& plan,
-                            hipStream_t stream) {
+                            int32_t* expert_ids, uint32_t* stats, uint32_t* scales,
+                            uint32_t align, const int32_t* ids, int64_t N, int32_t E,
+                            void* workspace, const IndexPlan& plan, hipStream_t stream) {
   uint32_t* counts = static_cast<uint32_t*>(workspace);
   if (plan.waves == 16)
-    return launch_indices_t<16>(order, starts, restore, expert_ids, stats, ids, N, E, counts,
-                                plan, stream);
-  return launch_indices_t<4>(order, starts, restore, expert_ids, stats, ids, N, E, counts, plan,
-                             stream);
+    return launch_indices_t<16>(order, starts, restore, expert_ids, stats, scales, align, ids, N,
+                                E, counts, plan, stream);
+  return launch_indices_t<4>(order, starts, restore, expert_ids, stats, scales, align, ids, N, E,
+                             counts, plan, stream);
 }
 
 }  // namespace moe

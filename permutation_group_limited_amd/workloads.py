@@ -137,7 +137,7 @@ def random_bias(E: int, seed: int, std: float = 0.01, levels: int = 0) -> torch.
 def random_ids(N: int, E: int, seed: int, skew: float = 0.0) -> torch.Tensor:
     """Flat expert ids [N] int32; skew > 0 draws from a Zipf(skew)-like pmf."""
     g = torch.Generator().manual_seed(seed)
-    if skew > 0.0:
+    if skew > 0.0 and N > 0:
         p = torch.arange(1, E + 1, dtype=torch.float64).pow(-skew)
         return torch.multinomial(p / p.sum(), N, replacement=True, generator=g).to(torch.int32)
     return torch.randint(0, E, (N,), generator=g, dtype=torch.int32)

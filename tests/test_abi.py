@@ -137,3 +137,14 @@ def test_logits_router_validates_like_router(lib):
     # same shape checks as the plain router (E % n_groups != 0)
     assert lib.moe_router_group_limited_logits(FAKE, FAKE, FAKE, FAKE, 0, 0, 1, 4, 256, 8, 3, 1,
                                                1, ctypes.c_float(1.0), 0, None) == INVALID
+
+
+def test_aligned_indices_validation(lib):
+    args = [FAKE] * 6 + [100, 256, FAKE, 1 << 20]
+    assert lib.moe_create_indices_aligned(*args, None, 4, None) == INVALID  # no output
+    assert lib.moe_create_indices_aligned(*args, FAKE, 0, None) == INVALID  # align 0
+    big = [FAKE] * 6 + [(1 << 32) - 10, 256, FAKE, 1 << 30]
+    assert lib.moe_create_indices_aligned(*big, FAKE, 2, None) == INVALID  # padded total overflows
+    assert lib.moe_create_indices_aligned(*args, FAKE_ODD, 4, None) == ALIGNMENT
+    # the plain entry point still refuses scales_offset_p
+    assert lib.moe_create_indices(*args, FAKE, None) == UNSUPPORTED

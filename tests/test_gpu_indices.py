@@ -5,6 +5,7 @@ import pytest
 import torch
 
 import oracle
+from permutation_group_limited_amd import binding
 from permutation_group_limited_amd import workloads as wl
 
 from _gpu import assert_indices_equal, gpu_indices, log
@@ -84,3 +85,31 @@ def test_out_of_range_ids_stay_contained():
     # the valid slots keep their own (uncompacted) indices
     assert np.array_equal(got["token_expert_order"][:n], keep[ref["token_expert_order"]])
     assert np.array_equal(got["restore_token_order"][keep], ref["restore_token_order"])
+
+
+def gpu_indices_aligned(ids, E, align):
+    ids = torch.as_tensor(ids).reshape(-1).to(torch.int32)
+    n = ids.numel()
+    d = ids.to("cuda:0")
+    mk = lambda m: torch.full((m,), 0x5A5A5A5A, dtype=torch.int32, device="cuda:0")
+    order, restore, starts, eids, stats, scales = mk(n), mk(n), mk(E + 1), mk(E), mk(2), mk(E + 1)
+    ws = mk(max(binding.moe_create_indices_workspace_size(n, E), 4) // 4)
+    binding.moe_create_indices_aligned(order, starts, restore, eids, stats, d, ws, scales, align)
+    torch.cuda.synchronize()
+    return {"token_expert_order": order.cpu().numpy().view(np.uint32),
+            "expert_start_indices": starts.cpu().numpy().view(np.uint32),
+            "restore_token_order": restore.cpu().numpy().view(np.uint32),
+            "expert_ids": eids.cpu().numpy(),
+            "expert_usage_stats": stats.cpu().numpy().view(np.uint32)}, \
+        scales.cpu().numpy().view(np.uint32)
+
+
+@pytest.mark.parametrize("align", [1, 3, 32, 128])
+@pytest.mark.parametrize("N,E", [(0, 8), (100, 8), (1024, 256), (65536, 256), (524288, 256),
+                                 (5000, 1000)])
+def test_aligned_scale_offsets(N, E, align):
+    log("aligned indices N", N, "E", E, "align", align)
+    ids = wl.random_ids(N, E, seed=N + align, skew=1.2).numpy()
+    got, scales = gpu_indices_aligned(ids, E, align)
+    assert_indices_equal(got, oracle.create_indices(ids, E))
+    assert np.array_equal(scales, oracle.scale_offsets(ids, E, align))

@@ -124,3 +124,42 @@ def test_rejects_out_of_range_ids(oracle):
         oracle.create_indices(np.array([0, 8], np.int32), 8)
     with pytest.raises(ValueError):
         oracle.create_indices(np.array([-1], np.int32), 8)
+
+
+def padded_layout_offsets(ids, E, align):
+    """Operational definition: lay the active experts' rows out one after
+    another, appending padding rows after each until the length is a
+    multiple of align; record where each expert starts."""
+    rows = []
+    starts = []
+    for e in range(E):
+        n = int(np.sum(np.asarray(ids) == e))
+        if n == 0:
+            continue
+        starts.append(len(rows))
+        rows.extend([e] * n)
+        while len(rows) % align:
+            rows.append(-1)
+    return starts + [len(rows)] * (E + 1 - len(starts))
+
+
+@pytest.mark.parametrize("align", [1, 2, 3, 16, 128])
+@pytest.mark.parametrize("N,E,seed", [(0, 4, 0), (1, 4, 1), (37, 5, 2), (1000, 64, 3),
+                                      (4096, 256, 4)])
+def test_scale_offsets_by_layout(oracle, align, N, E, seed):
+    ids = wl.random_ids(N, E, seed=seed, skew=1.0 if seed % 2 else 0.0).numpy()
+    got = oracle.scale_offsets(ids, E, align)
+    assert got.tolist() == padded_layout_offsets(ids, E, align)
+    if align == 1:
+        assert np.array_equal(got, oracle.create_indices(ids, E)["expert_start_indices"])
+    d = np.diff(got.astype(np.int64))
+    assert np.all(d % align == 0) and np.all(d >= 0)
+
+
+def test_scale_offsets_fixture(oracle, golden_dir):
+    with open(os.path.join(golden_dir, "indices_worked_example.json")) as f:
+        fx = json.load(f)
+    a = fx["aligned_scale_offsets"]
+    ids = np.array(fx["topk_ids_2d"], np.int32)
+    assert oracle.scale_offsets(ids, fx["E"], a["scale_align"]).tolist() == a["scales_offset"]
+    assert oracle.scale_offsets(ids, fx["E"], 1).tolist() == fx["expert_start_indices"]

@@ -54,6 +54,10 @@ MUTATIONS = [
     ("inactive experts listed", INDICES,
      "if (count[e] > 0) {\n            expert_ids[active] = e;",
      "if (count[e] >= 0) {\n            expert_ids[active] = e;"),
+    ("scale offsets not padded", INDICES,
+     "offset += (count[e] + align - 1) / align * align;", "offset += count[e];"),
+    ("scale offsets rounded down", INDICES,
+     "offset += (count[e] + align - 1) / align * align;", "offset += count[e] / align * align;"),
     ("accumulator wider than fp32", FINALIZE,
      ["float* acc = (float*)malloc(sizeof(float)",
       "acc[h] = fmaf(w, load_as_f32(down, down_dtype, row * H + h), acc[h]);"],
