@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time for the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the side measurements (logits router, decode latency)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="after the run, copy BYTES with torch's plain copy kernel (3 times): "
                          "the reference dispatch for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE")
@@ -204,6 +206,9 @@ def main():
                      "traffic": traffic},
     }
 
+    if not args.no_extras:
+        result["extras"] = extras(wk, scores_h, bias_h, idx, wts, args.steps)
+
     if args.copy_probe > 0:
         src = torch.ones(args.copy_probe // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -218,6 +223,98 @@ def main():
             wk, scores_h, bias_h, down, idx, wts, order, restore, starts, eids, stats, out,
             args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def graph_replay_us(fn, reps=200):
+    """Mean GPU time of fn() captured once in a HIP graph and replayed."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(5):
+        g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps * 1e3
+
+
+def extras(wk, scores_h, bias_h, idx, wts, steps):
+    """Side measurements of the widened entry points:
+      * the router on logits (sigmoid computed in the kernel) against the
+        router on precomputed scores, same workload, K back-to-back launches;
+      * the decode-shaped workload (T=128): one whole step (router ->
+        create_indices -> finalize) captured in a HIP graph, mean replay time
+        (eager launches would measure the host, not the GPU)."""
+    import torch
+
+    from permutation_group_limited_amd import binding
+    from permutation_group_limited_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    res = {}
+    fn = binding.SCORE_SIGMOID if wk.score_fn == "sigmoid" else binding.SCORE_SOFTMAX
+    logits = wl.make_logits(wk).to(dev)
+    bias = bias_h.to(dev)
+
+    def run(f):
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            f()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    res["router_logits_ms"] = run(lambda: binding.moe_router_group_limited_logits(
+        idx, wts, logits, bias, fn, wk.n_groups, wk.topk_group, wk.norm_weights, wk.scale))
+    scores = scores_h.to(dev)
+    res["router_scores_ms"] = run(lambda: binding.moe_router_group_limited(
+        idx, wts, scores, bias, wk.n_groups, wk.topk_group, wk.norm_weights, wk.scale))
+
+    dk = wl.WORKLOADS["decode"]
+    T, E, K = dk.T, dk.E, dk.K
+    s = wl.make_scores(dk).to(dev)
+    b = wl.make_bias(dk).to(dev)
+    down = wl.make_down(dk, device=dev)
+    i2 = torch.empty(T, K, dtype=torch.int32, device=dev)
+    w2 = torch.empty(T, K, dtype=torch.float32, device=dev)
+    o2, r2 = (torch.empty(T * K, dtype=torch.int32, device=dev) for _ in range(2))
+    st2 = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    e2 = torch.empty(E, dtype=torch.int32, device=dev)
+    u2 = torch.empty(2, dtype=torch.int32, device=dev)
+    ws2 = torch.empty(max(binding.moe_create_indices_workspace_size(T * K, E), 4) // 4,
+                      dtype=torch.int32, device=dev)
+    out2 = torch.empty(T, dk.H, dtype=dk.out_dtype, device=dev)
+
+    def decode_step():
+        binding.moe_router_group_limited(i2, w2, s, b, dk.n_groups, dk.topk_group,
+                                         dk.norm_weights, dk.scale)
+        binding.moe_create_indices(o2, st2, r2, e2, u2, i2, ws2)
+        binding.moe_finalize(out2, down, r2, w2)
+
+    us = graph_replay_us(decode_step)
+    db = T * E * 4 + E * 4 + T * K * 8 + T * K * 12 + (2 * E + 1) * 4 + 8 + \
+        T * K * dk.H * 2 + T * K * 8 + T * dk.H * 2
+    res["decode"] = {"workload": dk.describe(), "us_per_step_graph": us,
+                     "token_slots_per_s": T * K / (us * 1e-6),
+                     "hbm_gbps": db / (us * 1e-6) / 1e9}
+    return res
 
 
 def cpu_leg(wk, scores_h, bias_h, down, idx, wts, order, restore, starts, eids, stats, out,
