@@ -225,8 +225,10 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def graph_replay_us(fn, reps=200):
-    """Mean GPU time of fn() captured once in a HIP graph and replayed."""
+def graph_replay_us(fn, per_graph=20, reps=50):
+    """Mean GPU time of one fn() call: per_graph calls captured back to back
+    in one HIP graph, the graph replayed reps times (a graph of one call
+    would mostly time the graph launch itself)."""
     import torch
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -236,8 +238,9 @@ def graph_replay_us(fn, reps=200):
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        fn()
-    for _ in range(5):
+        for _ in range(per_graph):
+            fn()
+    for _ in range(3):
         g.replay()
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
@@ -247,16 +250,18 @@ def graph_replay_us(fn, reps=200):
         g.replay()
     b.record()
     torch.cuda.synchronize()
-    return a.elapsed_time(b) / reps * 1e3
+    return a.elapsed_time(b) / (reps * per_graph) * 1e3
 
 
 def extras(wk, scores_h, bias_h, idx, wts, steps):
     """Side measurements of the widened entry points:
       * the router on logits (sigmoid computed in the kernel) against the
         router on precomputed scores, same workload, K back-to-back launches;
-      * the decode-shaped workload (T=128): one whole step (router ->
-        create_indices -> finalize) captured in a HIP graph, mean replay time
-        (eager launches would measure the host, not the GPU)."""
+      * the decode-shaped workload (T=128): whole steps (router ->
+        create_indices -> finalize) captured 20 to a HIP graph, mean GPU time
+        per step (eager launches would measure the host, not the GPU); the
+        same with router and index creation fused into one launch; and
+        router + index creation alone, separate and fused."""
     import torch
 
     from permutation_group_limited_amd import binding
@@ -309,10 +314,30 @@ def extras(wk, scores_h, bias_h, idx, wts, steps):
         binding.moe_finalize(out2, down, r2, w2)
 
     us = graph_replay_us(decode_step)
+    tk = torch.zeros(max(binding.moe_route_and_index_workspace_size(), 4) // 4,
+                     dtype=torch.int32, device=dev)
+
+    def decode_step_fused():
+        binding.moe_route_and_index(i2, w2, o2, st2, r2, e2, u2, s, b, tk, dk.n_groups,
+                                    dk.topk_group, dk.norm_weights, dk.scale)
+        binding.moe_finalize(out2, down, r2, w2)
+
+    us_fused = graph_replay_us(decode_step_fused)
+    us_ri_sep = graph_replay_us(lambda: (
+        binding.moe_router_group_limited(i2, w2, s, b, dk.n_groups, dk.topk_group,
+                                         dk.norm_weights, dk.scale),
+        binding.moe_create_indices(o2, st2, r2, e2, u2, i2, ws2)))
+    us_ri_fused = graph_replay_us(lambda: binding.moe_route_and_index(
+        i2, w2, o2, st2, r2, e2, u2, s, b, tk, dk.n_groups, dk.topk_group, dk.norm_weights,
+        dk.scale))
     db = T * E * 4 + E * 4 + T * K * 8 + T * K * 12 + (2 * E + 1) * 4 + 8 + \
         T * K * dk.H * 2 + T * K * 8 + T * dk.H * 2
     res["decode"] = {"workload": dk.describe(), "us_per_step_graph": us,
+                     "us_per_step_graph_fused": us_fused,
+                     "us_route_index_graph": us_ri_sep,
+                     "us_route_index_graph_fused": us_ri_fused,
                      "token_slots_per_s": T * K / (us * 1e-6),
+                     "token_slots_per_s_fused": T * K / (us_fused * 1e-6),
                      "hbm_gbps": db / (us * 1e-6) / 1e9}
     return res
 

@@ -108,6 +108,7 @@ moe_status_t moe_router_group_limited(int32_t* expert_indices, void* expert_weig
 
 /* Score functions the logits entry point applies before routing. */
 typedef enum {
+    MOE_SCORE_NONE = 0,    /* the input already holds the scores */
     MOE_SCORE_SIGMOID = 1, /* score = 1 / (1 + exp(-logit)) */
     MOE_SCORE_SOFTMAX = 2  /* score = softmax of the token's E logits */
 } moe_score_fn_t;
@@ -204,6 +205,58 @@ moe_status_t moe_create_indices_aligned(uint32_t* token_expert_order,
                                         int64_t N, int32_t E, void* workspace,
                                         size_t workspace_bytes, uint32_t* scales_offset,
                                         uint32_t scale_align, void* stream);
+
+/*
+ * moe_route_and_index_workspace_size
+ * Bytes of device workspace moe_route_and_index needs: one uint32 counter.
+ * Pure host computation; never fails.
+ */
+size_t moe_route_and_index_workspace_size(void);
+
+/*
+ * moe_route_and_index
+ * The router (moe_router_group_limited, or moe_router_group_limited_logits
+ * when score_fn is not MOE_SCORE_NONE) and moe_create_indices_aligned /
+ * moe_create_indices on its expert_indices, in one kernel launch, for
+ * small batches where the gap between two launches is a large part of the
+ * routing time. Every output is bit-identical to what the two separate
+ * calls produce on the same inputs.
+ *
+ *   expert_indices, expert_weights       out as moe_router_group_limited.
+ *   token_expert_order ... expert_usage_stats
+ *                                        out as moe_create_indices, with
+ *                                        N = T * K.
+ *   scales_offset, scale_align           as moe_create_indices_aligned;
+ *                                        scales_offset may be NULL (no
+ *                                        aligned offsets, scale_align
+ *                                        ignored).
+ *   router_input     in [T, E], input_dtype: scores (score_fn =
+ *                    MOE_SCORE_NONE) or logits (MOE_SCORE_SIGMOID /
+ *                    MOE_SCORE_SOFTMAX).
+ *   expert_bias, scalars                 as moe_router_group_limited.
+ *   workspace        device buffer of at least
+ *                    moe_route_and_index_workspace_size() bytes, 4-byte
+ *                    aligned, ZERO-FILLED before its first use; every call
+ *                    leaves it zero again. Calls that share a workspace
+ *                    must not run concurrently (one stream, or ordered
+ *                    streams).
+ *
+ * Validation: that of the two separate calls, plus T * K <= 16384 (larger
+ * batches give MOE_ERR_UNSUPPORTED: the index step runs on one workgroup,
+ * and the separate calls are faster there). With T = 0 only the index
+ * metadata outputs are written, as moe_create_indices does for N = 0.
+ */
+moe_status_t moe_route_and_index(int32_t* expert_indices, void* expert_weights,
+                                 uint32_t* token_expert_order, uint32_t* expert_start_indices,
+                                 uint32_t* restore_token_order, int32_t* expert_ids,
+                                 uint32_t* expert_usage_stats, uint32_t* scales_offset,
+                                 uint32_t scale_align, const void* router_input,
+                                 const void* expert_bias, moe_dtype_t input_dtype,
+                                 moe_dtype_t bias_dtype, moe_score_fn_t score_fn, int64_t T,
+                                 int32_t E, int32_t K, int32_t n_groups, int32_t topk_group,
+                                 int32_t norm_weights, float routed_scaling_factor,
+                                 moe_group_score_t group_score, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 /*
  * moe_finalize

@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     DTYPE_F32,
     GROUP_MAX,
     GROUP_TOP2_SUM,
+    SCORE_NONE,
     SCORE_SIGMOID,
     SCORE_SOFTMAX,
     MoeError,
@@ -20,6 +21,8 @@ from .binding import (  # noqa: F401
     moe_create_indices_aligned,
     moe_create_indices_workspace_size,
     moe_finalize,
+    moe_route_and_index,
+    moe_route_and_index_workspace_size,
     moe_router_group_limited,
     moe_router_group_limited_logits,
 )

@@ -26,6 +26,7 @@ DTYPE_BF16 = 1
 DTYPE_F16 = 2
 GROUP_TOP2_SUM = 0
 GROUP_MAX = 1
+SCORE_NONE = 0
 SCORE_SIGMOID = 1
 SCORE_SOFTMAX = 2
 
@@ -87,6 +88,12 @@ def load_library(check_runtime: bool = True):
     lib.moe_create_indices_aligned.argtypes = [p, p, p, p, p, p, i64, i32, p, ctypes.c_size_t, p,
                                                ctypes.c_uint32, p]
     lib.moe_create_indices_aligned.restype = ctypes.c_int
+    lib.moe_route_and_index_workspace_size.argtypes = []
+    lib.moe_route_and_index_workspace_size.restype = ctypes.c_size_t
+    lib.moe_route_and_index.argtypes = [p, p, p, p, p, p, p, p, ctypes.c_uint32, p, p, i32, i32,
+                                        i32, i64, i32, i32, i32, i32, i32, ctypes.c_float, i32,
+                                        p, ctypes.c_size_t, p]
+    lib.moe_route_and_index.restype = ctypes.c_int
     lib.moe_finalize.argtypes = [p, i32, p, i32, p, p, i32, i64, i32, i64, p]
     lib.moe_finalize.restype = ctypes.c_int
     lib.moe_status_string.argtypes = [i32]
@@ -259,6 +266,64 @@ def moe_create_indices_aligned(token_expert_order: torch.Tensor,
         _ptr(expert_ids), _ptr(expert_usage_stats), _ptr(topk_ids), n, E, _ptr(workspace),
         ws_bytes, _ptr(scales_offset), int(scale_align), _stream(stream, topk_ids, expert_ids))
     _check("moe_create_indices_aligned", st)
+
+
+def moe_route_and_index_workspace_size() -> int:
+    """Device workspace bytes moe_route_and_index needs (one counter)."""
+    return int(load_library().moe_route_and_index_workspace_size())
+
+
+def moe_route_and_index(expert_indices: torch.Tensor, expert_weights: torch.Tensor,
+                        token_expert_order: torch.Tensor, expert_start_indices: torch.Tensor,
+                        restore_token_order: torch.Tensor, expert_ids: torch.Tensor,
+                        expert_usage_stats: torch.Tensor, router_input: torch.Tensor,
+                        expert_bias: torch.Tensor, workspace: torch.Tensor, n_groups: int,
+                        topk_group: int, norm_weights: bool, routed_scaling_factor: float,
+                        group_score: int = GROUP_TOP2_SUM, score_fn: int = SCORE_NONE,
+                        scales_offset: torch.Tensor = None, scale_align: int = 0,
+                        stream=None) -> None:
+    """Router and index creation in one launch (T * K <= 16384). router_input
+    [T, E] holds scores (score_fn SCORE_NONE) or logits; the outputs are those
+    of moe_router_group_limited(_logits) and moe_create_indices(_aligned).
+    workspace: at least moe_route_and_index_workspace_size() bytes, zero
+    before the first call (each call leaves it zero)."""
+    lib = load_library()
+    _dev(expert_indices, expert_weights, token_expert_order, expert_start_indices,
+         restore_token_order, expert_ids, expert_usage_stats, router_input, expert_bias,
+         workspace, scales_offset)
+    T, E = router_input.shape
+    K = expert_indices.shape[1]
+    if expert_indices.dtype != torch.int32 or tuple(expert_indices.shape) != (T, K):
+        raise ValueError("expert_indices must be int32 [T, K]")
+    if tuple(expert_weights.shape) != (T, K) or expert_weights.dtype != router_input.dtype:
+        raise ValueError("expert_weights must be [T, K] with the router input's dtype")
+    if tuple(expert_bias.shape) != (E,):
+        raise ValueError("expert_bias must be [E]")
+    for t, name in ((token_expert_order, "token_expert_order"),
+                    (expert_start_indices, "expert_start_indices"),
+                    (restore_token_order, "restore_token_order"), (expert_ids, "expert_ids"),
+                    (expert_usage_stats, "expert_usage_stats")):
+        _int32_like(t, name)
+    if scales_offset is not None:
+        _int32_like(scales_offset, "scales_offset")
+        if scales_offset.numel() != E + 1:
+            raise ValueError("scales_offset needs E+1 entries")
+    n = T * K
+    if token_expert_order.numel() != n or restore_token_order.numel() != n:
+        raise ValueError("token_expert_order and restore_token_order need T*K entries")
+    if expert_start_indices.numel() != E + 1 or expert_ids.numel() != E or \
+            expert_usage_stats.numel() != 2:
+        raise ValueError("expert_start_indices needs E+1 entries, expert_ids E, "
+                         "expert_usage_stats 2")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.moe_route_and_index(
+        _ptr(expert_indices), _ptr(expert_weights), _ptr(token_expert_order),
+        _ptr(expert_start_indices), _ptr(restore_token_order), _ptr(expert_ids),
+        _ptr(expert_usage_stats), _ptr(scales_offset), int(scale_align), _ptr(router_input),
+        _ptr(expert_bias), _dtype_code(router_input), _dtype_code(expert_bias), int(score_fn), T,
+        E, K, n_groups, topk_group, int(bool(norm_weights)), ctypes.c_float(routed_scaling_factor),
+        int(group_score), _ptr(workspace), ws_bytes, _stream(stream, router_input))
+    _check("moe_route_and_index", st)
 
 
 def moe_finalize(output: torch.Tensor, down: torch.Tensor, restore_order: torch.Tensor,

@@ -8,41 +8,65 @@ kernels is an explicit fmaf), packed-fp32 instruction selection disabled.
 from __future__ import annotations
 
 import os
+import shutil
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmoe_route.so")
-SOURCES = ["api.hip", "router.hip", "indices.hip", "finalize.hip"]
+SOURCES = ["api.hip", "router.hip", "indices.hip", "finalize.hip", "route_index.hip",
+           "route_index_f32.hip", "route_index_bf16.hip", "route_index_f16.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + ["-I", INCLUDE, "-I", CSRC] + \
-        [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the packed-fp32 target feature and says so
     noise = "is not a recognized feature for this target"
-    msgs = [l for l in (r.stderr or "").splitlines() if noise not in l and "(ignoring feature)" not in l]
-    if r.returncode != 0:
-        sys.stderr.write("\n".join(msgs) + "\n")
-        raise RuntimeError("hipcc failed building %s" % LIB)
-    if verbose and msgs:
-        sys.stderr.write("\n".join(msgs) + "\n")
-    os.replace(tmp, LIB)
+    msgs = [l for l in (r.stderr or "").splitlines()
+            if noise not in l and "(ignoring feature)" not in l]
+    return r.returncode, msgs
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link."""
+    tmpdir = tempfile.mkdtemp(prefix="moe_build_")
+    try:
+        objs = [os.path.join(tmpdir, s.replace(".hip", ".o")) for s in SOURCES]
+        cmds = [[HIPCC] + FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, s),
+                                   "-o", o] for s, o in zip(SOURCES, objs)]
+        jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+        with ThreadPoolExecutor(jobs) as ex:
+            results = list(ex.map(lambda c: _run(c, verbose), cmds))
+        for (rc, msgs), src in zip(results, SOURCES):
+            if rc != 0:
+                sys.stderr.write("\n".join(msgs) + "\n")
+                raise RuntimeError("hipcc failed compiling %s" % src)
+            if verbose and msgs:
+                sys.stderr.write("\n".join(msgs) + "\n")
+        tmp = LIB + ".tmp%d" % os.getpid()
+        rc, msgs = _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs +
+                        ["-o", tmp], verbose)
+        if rc != 0:
+            sys.stderr.write("\n".join(msgs) + "\n")
+            raise RuntimeError("hipcc failed linking %s" % LIB)
+        os.replace(tmp, LIB)
+    finally:
+        shutil.rmtree(tmpdir, ignore_errors=True)
     return LIB
 
 

@@ -37,13 +37,11 @@ using namespace moe;
 
 extern "C" {
 
-static moe_status_t router_common(int32_t* expert_indices, void* expert_weights,
-                                  const void* expert_scores, const void* expert_bias,
-                                  moe_dtype_t scores_dtype, moe_dtype_t bias_dtype,
-                                  int32_t score_fn, int64_t T, int32_t E, int32_t K,
-                                  int32_t n_groups, int32_t topk_group, int32_t norm_weights,
-                                  float routed_scaling_factor, moe_group_score_t group_score,
-                                  void* stream) {
+static moe_status_t router_check(int32_t* expert_indices, void* expert_weights,
+                                 const void* expert_scores, const void* expert_bias,
+                                 moe_dtype_t scores_dtype, moe_dtype_t bias_dtype, int64_t T,
+                                 int32_t E, int32_t K, int32_t n_groups, int32_t topk_group,
+                                 moe_group_score_t group_score) {
   if (T < 0 || E < 1 || n_groups < 1 || n_groups > 64 || E % n_groups != 0)
     return MOE_ERR_INVALID_ARG;
   if (topk_group < 1 || topk_group > n_groups) return MOE_ERR_INVALID_ARG;
@@ -60,7 +58,20 @@ static moe_status_t router_common(int32_t* expert_indices, void* expert_weights,
   if (!aligned(expert_scores, 16) || !aligned(expert_bias, 16) || !aligned(expert_indices, 4) ||
       !aligned(expert_weights, dtype_bytes(scores_dtype)))
     return MOE_ERR_ALIGNMENT;
-  if (T == 0) return MOE_OK;
+  return MOE_OK;
+}
+
+static moe_status_t router_common(int32_t* expert_indices, void* expert_weights,
+                                  const void* expert_scores, const void* expert_bias,
+                                  moe_dtype_t scores_dtype, moe_dtype_t bias_dtype,
+                                  int32_t score_fn, int64_t T, int32_t E, int32_t K,
+                                  int32_t n_groups, int32_t topk_group, int32_t norm_weights,
+                                  float routed_scaling_factor, moe_group_score_t group_score,
+                                  void* stream) {
+  const moe_status_t st = router_check(expert_indices, expert_weights, expert_scores, expert_bias,
+                                       scores_dtype, bias_dtype, T, E, K, n_groups, topk_group,
+                                       group_score);
+  if (st != MOE_OK || T == 0) return st;
   return launch_router(expert_indices, expert_weights, expert_scores, expert_bias, scores_dtype,
                        bias_dtype, score_fn, T, E, K, n_groups, topk_group, norm_weights ? 1 : 0,
                        routed_scaling_factor, static_cast<int32_t>(group_score),
@@ -97,12 +108,14 @@ size_t moe_create_indices_workspace_size(int64_t N, int32_t E) {
   return plan_indices(N, E).workspace_bytes;
 }
 
-static moe_status_t indices_common(uint32_t* token_expert_order,
-                                   uint32_t* expert_start_indices, uint32_t* restore_token_order,
-                                   int32_t* expert_ids, uint32_t* expert_usage_stats,
-                                   const int32_t* topk_ids, int64_t N, int32_t E,
-                                   void* workspace, size_t workspace_bytes,
-                                   uint32_t* scales_offset, uint32_t scale_align, void* stream) {
+// Index-output checks shared by the index entry points and the fused one
+// (which has no topk_ids input: pass a non-NULL stand-in).
+static moe_status_t index_outputs_check(uint32_t* token_expert_order,
+                                        uint32_t* expert_start_indices,
+                                        uint32_t* restore_token_order, int32_t* expert_ids,
+                                        uint32_t* expert_usage_stats, const int32_t* topk_ids,
+                                        int64_t N, int32_t E, uint32_t* scales_offset,
+                                        uint32_t scale_align) {
   if (N < 0 || N > (int64_t)UINT32_MAX || E < 1 || E > 1024) return MOE_ERR_INVALID_ARG;
   if (!expert_start_indices || !expert_ids || !expert_usage_stats) return MOE_ERR_INVALID_ARG;
   if (N > 0 && (!token_expert_order || !restore_token_order || !topk_ids))
@@ -110,14 +123,28 @@ static moe_status_t indices_common(uint32_t* token_expert_order,
   if (scales_offset != nullptr &&
       (scale_align == 0 || N + static_cast<int64_t>(E) * (scale_align - 1) > (int64_t)UINT32_MAX))
     return MOE_ERR_INVALID_ARG;
+  if (!aligned(token_expert_order, 4) || !aligned(expert_start_indices, 4) ||
+      !aligned(restore_token_order, 4) || !aligned(expert_ids, 4) ||
+      !aligned(expert_usage_stats, 4) || !aligned(topk_ids, 4) || !aligned(scales_offset, 4))
+    return MOE_ERR_ALIGNMENT;
+  return MOE_OK;
+}
+
+static moe_status_t indices_common(uint32_t* token_expert_order,
+                                   uint32_t* expert_start_indices, uint32_t* restore_token_order,
+                                   int32_t* expert_ids, uint32_t* expert_usage_stats,
+                                   const int32_t* topk_ids, int64_t N, int32_t E,
+                                   void* workspace, size_t workspace_bytes,
+                                   uint32_t* scales_offset, uint32_t scale_align, void* stream) {
+  const moe_status_t st =
+      index_outputs_check(token_expert_order, expert_start_indices, restore_token_order,
+                          expert_ids, expert_usage_stats, topk_ids, N, E, scales_offset,
+                          scale_align);
+  if (st != MOE_OK) return st;
   const IndexPlan plan = plan_indices(N, E);
   if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
     return MOE_ERR_WORKSPACE;
-  if (!aligned(workspace, 4) || !aligned(token_expert_order, 4) ||
-      !aligned(expert_start_indices, 4) || !aligned(restore_token_order, 4) ||
-      !aligned(expert_ids, 4) || !aligned(expert_usage_stats, 4) || !aligned(topk_ids, 4) ||
-      !aligned(scales_offset, 4))
-    return MOE_ERR_ALIGNMENT;
+  if (!aligned(workspace, 4)) return MOE_ERR_ALIGNMENT;
   return launch_indices(token_expert_order, expert_start_indices, restore_token_order, expert_ids,
                         expert_usage_stats, scales_offset, scale_align, topk_ids, N, E,
                         workspace, plan, static_cast<hipStream_t>(stream));
@@ -145,6 +172,48 @@ moe_status_t moe_create_indices_aligned(uint32_t* token_expert_order,
   return indices_common(token_expert_order, expert_start_indices, restore_token_order,
                         expert_ids, expert_usage_stats, topk_ids, N, E, workspace,
                         workspace_bytes, scales_offset, scale_align, stream);
+}
+
+size_t moe_route_and_index_workspace_size(void) { return sizeof(uint32_t); }
+
+moe_status_t moe_route_and_index(int32_t* expert_indices, void* expert_weights,
+                                 uint32_t* token_expert_order, uint32_t* expert_start_indices,
+                                 uint32_t* restore_token_order, int32_t* expert_ids,
+                                 uint32_t* expert_usage_stats, uint32_t* scales_offset,
+                                 uint32_t scale_align, const void* router_input,
+                                 const void* expert_bias, moe_dtype_t input_dtype,
+                                 moe_dtype_t bias_dtype, moe_score_fn_t score_fn, int64_t T,
+                                 int32_t E, int32_t K, int32_t n_groups, int32_t topk_group,
+                                 int32_t norm_weights, float routed_scaling_factor,
+                                 moe_group_score_t group_score, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (score_fn != MOE_SCORE_NONE && score_fn != MOE_SCORE_SIGMOID &&
+      score_fn != MOE_SCORE_SOFTMAX)
+    return MOE_ERR_INVALID_ARG;
+  moe_status_t st = router_check(expert_indices, expert_weights, router_input, expert_bias,
+                                 input_dtype, bias_dtype, T, E, K, n_groups, topk_group,
+                                 group_score);
+  if (st != MOE_OK) return st;
+  const int64_t N = T * K;  // < 2^32 after router_check
+  st = index_outputs_check(token_expert_order, expert_start_indices, restore_token_order,
+                           expert_ids, expert_usage_stats, expert_indices, N, E, scales_offset,
+                           scale_align);
+  if (st != MOE_OK) return st;
+  if (workspace == nullptr || workspace_bytes < sizeof(uint32_t)) return MOE_ERR_WORKSPACE;
+  if (!aligned(workspace, 4)) return MOE_ERR_ALIGNMENT;
+  if (N > kRouteIndexMaxSlots) return MOE_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0)  // nothing to route: the index step alone writes the metadata
+    return launch_indices(token_expert_order, expert_start_indices, restore_token_order,
+                          expert_ids, expert_usage_stats, scales_offset, scale_align,
+                          expert_indices, 0, E, nullptr, plan_indices(0, E), s);
+  return launch_route_index(expert_indices, expert_weights, router_input, expert_bias,
+                            input_dtype, bias_dtype, static_cast<int32_t>(score_fn), T, E, K,
+                            n_groups, topk_group, norm_weights ? 1 : 0, routed_scaling_factor,
+                            static_cast<int32_t>(group_score), token_expert_order,
+                            expert_start_indices, restore_token_order, expert_ids,
+                            expert_usage_stats, scales_offset, scale_align,
+                            static_cast<uint32_t*>(workspace), s);
 }
 
 moe_status_t moe_finalize(void* output, moe_dtype_t out_dtype, const void* down,

@@ -1,0 +1,14 @@
+// Instances of the fused router + index kernel for bf16 scores with bf16 or fp32 bias.
+#include "route_index_impl.hpp"
+
+namespace moe {
+template moe_status_t launch_route_index_dt<DBF16, DBF16>(int32_t, int32_t, int32_t*, void*,
+                                                   const void*, const void*, int64_t, int32_t,
+                                                   int32_t, int32_t, int32_t, float, int32_t,
+                                                   IndexOutputs, uint32_t*, hipStream_t);
+template moe_status_t launch_route_index_dt<DBF16, DF32>(int32_t, int32_t, int32_t*, void*,
+                                                   const void*, const void*, int64_t, int32_t,
+                                                   int32_t, int32_t, int32_t, float, int32_t,
+                                                   IndexOutputs, uint32_t*, hipStream_t);
+
+}  // namespace moe

@@ -22,170 +22,10 @@
 //    lower-index tie rule) and pops its head. Round k fills slot k, so the
 //    slots come out in (score desc, id asc) order.
 //  * weights: the K winners' unbiased scores, summed in slot order.
-#include "common.hpp"
+#include "router_tokens.hpp"
 
 namespace moe {
 namespace {
-
-// Load EPL consecutive elements of dtype D (one vector load of EPL * size
-// bytes when that is 4, 8 or a multiple of 16) and widen them to fp32.
-template <typename D, int EPL>
-__device__ __forceinline__ void load_row(float (&dst)[EPL],
-                                         const typename D::storage* __restrict__ p) {
-  constexpr int kBytes = EPL * D::kBytes;
-  if constexpr (kBytes == 2) {
-    dst[0] = D::widen_bits(static_cast<uint32_t>(p[0]));
-  } else {
-    constexpr int kWords = kBytes / 4;
-    uint32_t w[kWords];
-    if constexpr (kBytes % 16 == 0) {
-#pragma unroll
-      for (int q = 0; q < kWords; q += 4) {
-        const u32x4 v = reinterpret_cast<const u32x4*>(p)[q / 4];
-        w[q] = v.x;
-        w[q + 1] = v.y;
-        w[q + 2] = v.z;
-        w[q + 3] = v.w;
-      }
-    } else if constexpr (kBytes == 8) {
-      const u32x2 v = *reinterpret_cast<const u32x2*>(p);
-      w[0] = v.x;
-      w[1] = v.y;
-    } else {
-      w[0] = *reinterpret_cast<const uint32_t*>(p);
-    }
-    if constexpr (D::kBytes == 4) {
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) dst[i] = D::widen_bits(w[i]);
-    } else {
-#pragma unroll
-      for (int q = 0; q < kWords; ++q) {
-        dst[2 * q] = D::widen_bits(w[q] & 0xFFFFu);
-        dst[2 * q + 1] = D::widen_hi(w[q]);
-      }
-    }
-  }
-}
-
-// Cross-lane moves inside rows of 16 lanes. Every control used here reads a
-// lane of the same row, so no lane is left without a source; the moves are
-// written so that the compiler can fold them into the consuming VALU op.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
-  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), CTRL, 0xF, 0xF, true));
-}
-constexpr int kXor1 = 0xB1;        // quad_perm [1,0,3,2]
-constexpr int kXor2 = 0x4E;        // quad_perm [2,3,0,1]
-constexpr int kHalfMirror = 0x141;  // lane i <-> 7-i within each 8 lanes
-constexpr int kMirror = 0x140;      // lane i <-> 15-i within each row
-
-// Merge the (largest, second largest) pair of this lane with the pair of
-// the lane that holds a disjoint set of experts.
-__device__ __forceinline__ void merge_top2(float& m1, float& m2, float o1, float o2) {
-  const float n2 = fmaxf(fminf(m1, o1), fmaxf(m2, o2));
-  m1 = fmaxf(m1, o1);
-  m2 = n2;
-}
-
-// Top-2 over groups of `lpg` adjacent lanes (lpg a power of two, groups
-// aligned). Each step pairs lanes whose partial results cover disjoint
-// experts: xor 1 and xor 2 (quad_perm), then the mirrored half-row and row
-// (every lane of a quad, resp. half-row, already holds the same pair), then
-// xor 16 (ds_swizzle) and xor 32 (ds_bpermute).
-__device__ __forceinline__ void group_top2(float& m1, float& m2, int lpg) {
-  if (lpg >= 2) merge_top2(m1, m2, dpp_f<kXor1>(m1), dpp_f<kXor1>(m2));
-  if (lpg >= 4) merge_top2(m1, m2, dpp_f<kXor2>(m1), dpp_f<kXor2>(m2));
-  if (lpg >= 8) merge_top2(m1, m2, dpp_f<kHalfMirror>(m1), dpp_f<kHalfMirror>(m2));
-  if (lpg >= 16) merge_top2(m1, m2, dpp_f<kMirror>(m1), dpp_f<kMirror>(m2));
-  if (lpg >= 32) {
-    const float o1 = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(m1), 0x401F));
-    const float o2 = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(m2), 0x401F));
-    merge_top2(m1, m2, o1, o2);
-  }
-  if (lpg >= 64) merge_top2(m1, m2, __shfl_xor(m1, 32, kWave), __shfl_xor(m2, 32, kWave));
-}
-
-__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
-
-// Sum over groups of `lpg` adjacent lanes, same lane pairing as group_top2.
-__device__ __forceinline__ int group_sum(int x, int lpg) {
-  if (lpg >= 2) x += __builtin_amdgcn_mov_dpp(x, kXor1, 0xF, 0xF, true);
-  if (lpg >= 4) x += __builtin_amdgcn_mov_dpp(x, kXor2, 0xF, 0xF, true);
-  if (lpg >= 8) x += __builtin_amdgcn_mov_dpp(x, kHalfMirror, 0xF, 0xF, true);
-  if (lpg >= 16) x += __builtin_amdgcn_mov_dpp(x, kMirror, 0xF, 0xF, true);
-  if (lpg >= 32) x += __builtin_amdgcn_ds_swizzle(x, 0x401F);
-  if (lpg >= 64) x += __shfl_xor(x, 32, kWave);
-  return x;
-}
-
-// Maximum of v over the token's LPT lanes, returned to every lane of the
-// segment: xor 1 and xor 2 inside quads, mirrored half-rows and rows (by
-// then each quad, resp. half-row, is uniform), xor 16 by ds_swizzle; for a
-// full wave the four row maxima are combined through v_readlane.
-template <int LPT>
-__device__ __forceinline__ uint32_t segment_max(uint32_t v) {
-  if (LPT >= 2) v = umax(v, dpp_u<kXor1>(v));
-  if (LPT >= 4) v = umax(v, dpp_u<kXor2>(v));
-  if (LPT >= 8) v = umax(v, dpp_u<kHalfMirror>(v));
-  if (LPT >= 16) v = umax(v, dpp_u<kMirror>(v));
-  if constexpr (LPT == 32) {
-    v = umax(v, static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), 0x401F)));
-  } else if constexpr (LPT == kWave) {
-    const int x = static_cast<int>(v);
-    v = umax(umax(static_cast<uint32_t>(__builtin_amdgcn_readlane(x, 0)),
-                  static_cast<uint32_t>(__builtin_amdgcn_readlane(x, 16))),
-             umax(static_cast<uint32_t>(__builtin_amdgcn_readlane(x, 32)),
-                  static_cast<uint32_t>(__builtin_amdgcn_readlane(x, 48))));
-  }
-  return v;
-}
-
-// Stable descending sort of keys held in registers, carrying each key's
-// element index along: adjacent exchanges that swap only on a strictly
-// larger key keep equal keys in ascending element order.
-template <int EPL>
-__device__ __forceinline__ void sort_desc(uint32_t (&k)[EPL], uint32_t (&e)[EPL]) {
-#pragma unroll
-  for (int i = 1; i < EPL; ++i) {
-#pragma unroll
-    for (int j = i; j > 0; --j) {
-      const bool sw = k[j] > k[j - 1];
-      const uint32_t k0 = sw ? k[j] : k[j - 1], k1 = sw ? k[j - 1] : k[j];
-      const uint32_t e0 = sw ? e[j] : e[j - 1], e1 = sw ? e[j - 1] : e[j];
-      k[j - 1] = k0;
-      k[j] = k1;
-      e[j - 1] = e0;
-      e[j] = e1;
-    }
-  }
-}
-
-// Score functions applied to logits before routing (the page's optional
-// scores_input_fn): evaluated in binary64, rounded once to binary32.
-constexpr int kScoreLoad = 0;
-constexpr int kScoreSigmoid = 1;
-constexpr int kScoreSoftmax = 2;
-
-__device__ __forceinline__ float sigmoid_f64(float x) {
-  return static_cast<float>(1.0 / (1.0 + exp(-static_cast<double>(x))));
-}
-
-__device__ __forceinline__ float key_to_float(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
-}
-
-// Sum of v over the token's LPT lanes (xor butterfly; every lane of the
-// segment ends with the same value because each pairwise add is commutative).
-template <int LPT>
-__device__ __forceinline__ double segment_sum_f64(double v) {
-#pragma unroll
-  for (int off = 1; off < LPT; off <<= 1) v += __shfl_xor(v, off, kWave);
-  return v;
-}
 
 template <typename DS, typename DB, int EPL, int LPT, int FN>
 __global__ __launch_bounds__(kBlock) void router_kernel(
@@ -193,201 +33,25 @@ __global__ __launch_bounds__(kBlock) void router_kernel(
     const typename DS::storage* __restrict__ scores, const typename DB::storage* __restrict__ bias,
     int64_t T, int32_t K, int32_t n_groups, int32_t topk_group, int32_t norm_weights,
     float scale, int32_t mode) {
-  constexpr int E = EPL * LPT;
-  constexpr int TPW = kWave / LPT;  // tokens per wave
-  const int lane = lane_id();
-  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
-  const int sub = lane & (LPT - 1);
-  const int tok_lane0 = lane & ~(LPT - 1);
-  const int64_t t =
-      (static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave) * TPW + lane / LPT;
-  const bool tok_ok = t < T;
-  const int e0 = sub * EPL;
-  const uint64_t segmask =
-      (LPT == kWave) ? ~0ull : (((1ull << LPT) - 1ull) << tok_lane0);
-
-  float s[EPL], bi[EPL], b[EPL];
-  if (tok_ok) {
-    load_row<DS, EPL>(s, scores + t * E + e0);
-  } else {
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) s[i] = 0.0f;
-  }
-  load_row<DB, EPL>(bi, bias + e0);
-  // scores from logits (FN != kScoreLoad)
-  double sm_max = 0.0, sm_sum = 1.0;
-  if constexpr (FN == kScoreSigmoid) {
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) s[i] = sigmoid_f64(s[i]);
-  } else if constexpr (FN == kScoreSoftmax) {
-    uint32_t km = 0;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) km = umax(km, ordered_key(s[i]));
-    sm_max = static_cast<double>(key_to_float(segment_max<LPT>(km)));
-    double ex[EPL], part = 0.0;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      ex[i] = exp(static_cast<double>(s[i]) - sm_max);
-      part += ex[i];
-    }
-    sm_sum = segment_sum_f64<LPT>(part);
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) s[i] = static_cast<float>(ex[i] / sm_sum);
-  }
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) b[i] = s[i] + bi[i];
-
-  // ---- group stage: keep the best topk_group groups ------------------------
-  bool kept = true;
-  if (topk_group < n_groups) {
-    // E, n_groups and EPL are powers of two: shifts, not divisions
-    const int lg_groups = __builtin_ctz(static_cast<uint32_t>(n_groups));
-    const int S = E >> lg_groups;
-    const int LPG = S / EPL;  // lanes per group, a power of two
-    const int lg_lpg = __builtin_ctz(static_cast<uint32_t>(LPG));
-    float m1 = -__builtin_inff(), m2 = -__builtin_inff();
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      m2 = fmaxf(m2, fminf(m1, b[i]));
-      m1 = fmaxf(m1, b[i]);
-    }
-    group_top2(m1, m2, LPG);
-    const float gs = (mode == MOE_GROUP_MAX || S == 1) ? m1 : m1 + m2;
-    // rank of my group = groups that beat it; the LPG lanes of a group split
-    // the comparisons (lane q of the group tests groups q, q + LPG, ...) and
-    // add their counts
-    const int my_g = sub >> lg_lpg;
-    int beats = 0;
-    for (int j = sub & (LPG - 1); j < n_groups; j += LPG) {
-      const float o = __shfl(gs, tok_lane0 + j * LPG, kWave);
-      beats += (o > gs) || (o == gs && j < my_g);
-    }
-    kept = group_sum(beats, LPG) < topk_group;
-  }
-
-  // ---- top-K: K rounds of segment max over the lanes' sorted heads ---------
-  // Keys preserve the order of the biased scores (0 = not a candidate). Each
-  // lane sorts its EPL (key, element) pairs by key desc, element asc. A
-  // round takes the segment maximum of the lane heads; among lanes whose
-  // head equals it the lowest lane wins, which is the lowest expert id
-  // because lanes hold ascending, disjoint id ranges. The winner pops its
-  // head. Round k yields slot k.
-  uint32_t kv[EPL];
-  uint32_t ki[EPL];
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    kv[i] = (tok_ok && kept) ? ordered_key(b[i]) : 0u;
-    ki[i] = static_cast<uint32_t>(i);
-  }
-  sort_desc<EPL>(kv, ki);
-
-  uint32_t my_id = 0;
-  for (int k = 0; k < K; ++k) {
-    const uint32_t head = kv[0];
-    const uint64_t bal = __ballot(head == segment_max<LPT>(head)) & segmask;
-    const int win = __builtin_ctzll(static_cast<unsigned long long>(bal));
-    uint32_t id;
-    if constexpr (LPT == kWave) {
-      id = static_cast<uint32_t>(win * EPL) +
-           static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ki[0]), win));
-    } else {
-      id = static_cast<uint32_t>(win - tok_lane0);  // one expert per lane
-    }
-    if (sub == k) my_id = id;
-    if (lane == win) {
-#pragma unroll
-      for (int i = 0; i + 1 < EPL; ++i) {
-        kv[i] = kv[i + 1];
-        ki[i] = ki[i + 1];
-      }
-      kv[EPL - 1] = 0u;
-    }
-  }
-
-  // ---- weights from the unbiased scores -----------------------------------
-  const bool slot = tok_ok && sub < K;
-  if (my_id >= static_cast<uint32_t>(E)) my_id = 0;  // unreachable with finite scores
-  float u = 0.0f;
-  if (slot) {
-    u = load_f32<DS>(scores, t * E + my_id);
-    if constexpr (FN == kScoreSigmoid) u = sigmoid_f64(u);
-    if constexpr (FN == kScoreSoftmax)
-      u = static_cast<float>(exp(static_cast<double>(u) - sm_max) / sm_sum);
-  }
-  float w;
-  if (norm_weights) {
-    float d = 0.0f;
-    if constexpr (LPT == kWave) {
-      for (int q = 0; q < K; ++q)
-        d += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, u), q));
-    } else {
-      for (int q = 0; q < K; ++q) d += __shfl(u, tok_lane0 + q, kWave);
-    }
-    w = (u / d) * scale;
-  } else {
-    w = u * scale;
-  }
-  if (slot) {
-    out_idx[t * K + sub] = static_cast<int32_t>(my_id);
-    out_w[t * K + sub] = to_storage<DS>(w);
-  }
+  route_tokens<DS, DB, EPL, LPT, FN, kWavesPerBlock>(out_idx, out_w, scores, bias, T, K, n_groups,
+                                                     topk_group, norm_weights, scale, mode);
 }
 
 template <typename DS, typename DB, int EPL, int LPT, int FN>
-moe_status_t launch_router_t(int32_t* idx, void* w, const void* s, const void* b, int64_t T,
-                             int32_t K, int32_t G, int32_t TG, int32_t norm, float scale,
-                             int32_t mode, hipStream_t stream) {
-  constexpr int TPB = kWavesPerBlock * (kWave / LPT);  // tokens per block
-  const int64_t blocks = (T + TPB - 1) / TPB;
-  hipLaunchKernelGGL((router_kernel<DS, DB, EPL, LPT, FN>), dim3(static_cast<uint32_t>(blocks)),
-                     dim3(kBlock), 0, stream, idx, static_cast<typename DS::storage*>(w),
-                     static_cast<const typename DS::storage*>(s),
-                     static_cast<const typename DB::storage*>(b), T, K, G, TG, norm, scale, mode);
-  return check_launch();
-}
-
-template <typename DS, typename DB, int FN>
-moe_status_t launch_router_e(int32_t* idx, void* w, const void* s, const void* b, int64_t T,
-                             int32_t E, int32_t K, int32_t G, int32_t TG, int32_t norm,
-                             float scale, int32_t mode, hipStream_t stream) {
-#define MOE_R(EPL, LPT)                                                                     \
-  return launch_router_t<DS, DB, EPL, LPT, FN>(idx, w, s, b, T, K, G, TG, norm, scale, mode, \
-                                               stream)
-  switch (E) {
-    case 1: MOE_R(1, 1);
-    case 2: MOE_R(1, 2);
-    case 4: MOE_R(1, 4);
-    case 8: MOE_R(1, 8);
-    case 16: MOE_R(1, 16);
-    case 32: MOE_R(1, 32);
-    case 64: MOE_R(1, 64);
-    case 128: MOE_R(2, 64);
-    case 256: MOE_R(4, 64);
-    case 512: MOE_R(8, 64);
-    case 1024: MOE_R(16, 64);
-    default: return MOE_ERR_UNSUPPORTED;
+struct RouterLaunch {
+  static moe_status_t run(int32_t* idx, void* w, const void* s, const void* b, int64_t T,
+                          int32_t K, int32_t G, int32_t TG, int32_t norm, float scale,
+                          int32_t mode, hipStream_t stream) {
+    constexpr int TPB = kWavesPerBlock * (kWave / LPT);  // tokens per block
+    const int64_t blocks = (T + TPB - 1) / TPB;
+    hipLaunchKernelGGL((router_kernel<DS, DB, EPL, LPT, FN>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(kBlock), 0, stream, idx, static_cast<typename DS::storage*>(w),
+                       static_cast<const typename DS::storage*>(s),
+                       static_cast<const typename DB::storage*>(b), T, K, G, TG, norm, scale,
+                       mode);
+    return check_launch();
   }
-#undef MOE_R
-}
-
-template <typename DS, typename DB>
-moe_status_t launch_router_fn(int32_t* idx, void* w, const void* s, const void* b, int64_t T,
-                              int32_t E, int32_t K, int32_t G, int32_t TG, int32_t norm,
-                              float scale, int32_t mode, int32_t fn, hipStream_t stream) {
-  switch (fn) {
-    case kScoreLoad:
-      return launch_router_e<DS, DB, kScoreLoad>(idx, w, s, b, T, E, K, G, TG, norm, scale,
-                                                 mode, stream);
-    case kScoreSigmoid:
-      return launch_router_e<DS, DB, kScoreSigmoid>(idx, w, s, b, T, E, K, G, TG, norm, scale,
-                                                    mode, stream);
-    case kScoreSoftmax:
-      return launch_router_e<DS, DB, kScoreSoftmax>(idx, w, s, b, T, E, K, G, TG, norm, scale,
-                                                    mode, stream);
-    default:
-      return MOE_ERR_INVALID_ARG;
-  }
-}
+};
 
 }  // namespace
 
@@ -395,15 +59,8 @@ moe_status_t launch_router(int32_t* idx, void* w, const void* s, const void* b,
                            moe_dtype_t sd, moe_dtype_t bd, int32_t fn, int64_t T, int32_t E,
                            int32_t K, int32_t G, int32_t TG, int32_t norm, float scale,
                            int32_t mode, hipStream_t stream) {
-#define MOE_D(DS, DB) \
-  return launch_router_fn<DS, DB>(idx, w, s, b, T, E, K, G, TG, norm, scale, mode, fn, stream)
-  if (sd == MOE_DTYPE_F32 && bd == MOE_DTYPE_F32) MOE_D(DF32, DF32);
-  if (sd == MOE_DTYPE_BF16 && bd == MOE_DTYPE_BF16) MOE_D(DBF16, DBF16);
-  if (sd == MOE_DTYPE_BF16 && bd == MOE_DTYPE_F32) MOE_D(DBF16, DF32);
-  if (sd == MOE_DTYPE_F16 && bd == MOE_DTYPE_F16) MOE_D(DF16, DF16);
-  if (sd == MOE_DTYPE_F16 && bd == MOE_DTYPE_F32) MOE_D(DF16, DF32);
-#undef MOE_D
-  return MOE_ERR_UNSUPPORTED;
+  return dispatch_router<RouterLaunch>(sd, bd, fn, E, idx, w, s, b, T, K, G, TG, norm, scale,
+                                       mode, stream);
 }
 
 }  // namespace moe

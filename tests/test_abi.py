@@ -148,3 +148,45 @@ def test_aligned_indices_validation(lib):
     assert lib.moe_create_indices_aligned(*args, FAKE_ODD, 4, None) == ALIGNMENT
     # the plain entry point still refuses scales_offset_p
     assert lib.moe_create_indices(*args, FAKE, None) == UNSUPPORTED
+
+
+def route_index(lib, T=16, E=256, K=8, G=8, TG=4, fn=0, sd=0, bd=0, mode=0, ws=FAKE,
+                ws_bytes=4, scales=None, align=0, ptrs=None):
+    p = ptrs or (FAKE,) * 9
+    return lib.moe_route_and_index(p[0], p[1], p[2], p[3], p[4], p[5], p[6], scales, align,
+                                   p[7], p[8], sd, bd, fn, T, E, K, G, TG, 1,
+                                   ctypes.c_float(1.0), mode, ws, ws_bytes, None)
+
+
+def test_route_and_index_workspace_size(lib):
+    assert lib.moe_route_and_index_workspace_size() == 4
+
+
+@pytest.mark.parametrize("kw,code", [
+    # router checks
+    (dict(T=-1), INVALID), (dict(G=3), INVALID), (dict(K=0), INVALID), (dict(TG=9), INVALID),
+    (dict(mode=2), INVALID), (dict(fn=3), INVALID), (dict(sd=1, bd=2), UNSUPPORTED),
+    (dict(E=96, G=8), UNSUPPORTED), (dict(E=2048, G=8), UNSUPPORTED),
+    (dict(ptrs=(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE_MIS, FAKE)), ALIGNMENT),
+    (dict(ptrs=(None,) + (FAKE,) * 8), INVALID),
+    # index-output checks
+    (dict(ptrs=(FAKE, FAKE, None) + (FAKE,) * 6), INVALID),
+    (dict(ptrs=(FAKE, FAKE, FAKE, None) + (FAKE,) * 5), INVALID),
+    (dict(ptrs=(FAKE,) * 6 + (FAKE_ODD, FAKE, FAKE)), ALIGNMENT),
+    (dict(scales=FAKE, align=0), INVALID), (dict(scales=FAKE_ODD, align=4), ALIGNMENT),
+    # workspace
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=3), WORKSPACE), (dict(ws=FAKE_ODD), ALIGNMENT),
+    # batch size: the index step runs on one workgroup
+    (dict(T=2049, K=8), UNSUPPORTED), (dict(T=16385, E=8, G=1, TG=1, K=1), UNSUPPORTED),
+])
+def test_route_and_index_validation(lib, kw, code):
+    assert route_index(lib, **kw) == code
+
+
+def test_route_and_index_binding_rejects_host_tensors(lib):
+    z = torch.zeros
+    with pytest.raises(ValueError):
+        binding.moe_route_and_index(z(4, 2, dtype=torch.int32), z(4, 2), z(8, dtype=torch.int32),
+                                    z(9, dtype=torch.int32), z(8, dtype=torch.int32),
+                                    z(8, dtype=torch.int32), z(2, dtype=torch.int32), z(4, 8),
+                                    z(8), z(1, dtype=torch.int32), 1, 1, True, 1.0)

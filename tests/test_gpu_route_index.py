@@ -1,0 +1,243 @@
+"""GPU parity of moe_route_and_index (router and index creation in one
+launch) against the oracle's router followed by its index creation, and
+bit-identity with the two separate GPU entry points on the same inputs.
+
+Acceptance as for the separate stages: indices and every index output
+bit-exact; fp32 weights within 1e-6 relative, 16-bit weights within 1 ulp
+of the oracle and bit-identical to the separate router call. Marked gpu."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from permutation_group_limited_amd import binding
+from permutation_group_limited_amd import workloads as wl
+
+from _gpu import (DEV, assert_16bit_within_one_ulp, assert_indices_equal, assert_weights_close,
+                  bf16_bits, encode, log, to_np_u32)
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+FNS = {"none": (binding.SCORE_NONE, oracle.SCORE_LOAD),
+       "sigmoid": (binding.SCORE_SIGMOID, oracle.SCORE_SIGMOID),
+       "softmax": (binding.SCORE_SOFTMAX, oracle.SCORE_SOFTMAX)}
+POISON = 0x5A5A5A5A
+
+
+class Outputs:
+    """Device output buffers of one fused call, poisoned before the call."""
+
+    def __init__(self, T, E, K, dtype, aligned):
+        n = T * K
+        full = lambda *shape: torch.full(shape, POISON, dtype=torch.int32, device=DEV)  # noqa
+        self.idx = full(T, K)
+        self.w = torch.full((T, K), float("nan"), dtype=dtype, device=DEV)
+        self.order, self.restore = full(n), full(n)
+        self.starts, self.eids, self.stats = full(E + 1), full(E), full(2)
+        self.scales = full(E + 1) if aligned else None
+
+    def host(self):
+        wh = self.w.cpu()
+        return {
+            "idx": self.idx.cpu().numpy(),
+            "w": wh.numpy() if wh.dtype == torch.float32 else wh,
+            "ind": {"token_expert_order": to_np_u32(self.order),
+                    "expert_start_indices": to_np_u32(self.starts),
+                    "restore_token_order": to_np_u32(self.restore),
+                    "expert_ids": self.eids.cpu().numpy(),
+                    "expert_usage_stats": to_np_u32(self.stats)},
+            "scales": None if self.scales is None else to_np_u32(self.scales),
+        }
+
+
+def launch(o, x, b, ws, G, TG, norm, scale, fn, mode=0, align=0, stream=None):
+    binding.moe_route_and_index(o.idx, o.w, o.order, o.starts, o.restore, o.eids, o.stats, x, b,
+                                ws, G, TG, norm, scale, group_score=mode, score_fn=fn,
+                                scales_offset=o.scales, scale_align=align, stream=stream)
+
+
+def fused(x, b, K, G, TG, norm, scale, fn="none", mode=0, align=0, ws=None):
+    """One fused call on host inputs; checks the workspace is left zero."""
+    T, E = x.shape
+    o = Outputs(T, E, K, x.dtype, align > 0)
+    ws = torch.zeros(1, dtype=torch.int32, device=DEV) if ws is None else ws
+    launch(o, x.to(DEV), b.to(DEV), ws, G, TG, norm, scale, FNS[fn][0], mode, align)
+    torch.cuda.synchronize()
+    assert int(ws.item()) == 0, "workspace counter not left at zero"
+    return o.host()
+
+
+def separate(x, b, K, G, TG, norm, scale, fn="none", mode=0, align=0):
+    """The same step through the two separate entry points."""
+    T, E = x.shape
+    o = Outputs(T, E, K, x.dtype, align > 0)
+    xd, bd = x.to(DEV), b.to(DEV)
+    if fn == "none":
+        binding.moe_router_group_limited(o.idx, o.w, xd, bd, G, TG, norm, scale, mode)
+    else:
+        binding.moe_router_group_limited_logits(o.idx, o.w, xd, bd, FNS[fn][0], G, TG, norm,
+                                                scale, mode)
+    n = binding.moe_create_indices_workspace_size(T * K, E)
+    ws = torch.empty(max(n, 4) // 4, dtype=torch.int32, device=DEV)
+    if align:
+        binding.moe_create_indices_aligned(o.order, o.starts, o.restore, o.eids, o.stats, o.idx,
+                                           ws, o.scales, align)
+    else:
+        binding.moe_create_indices(o.order, o.starts, o.restore, o.eids, o.stats, o.idx, ws)
+    torch.cuda.synchronize()
+    return o.host()
+
+
+def check_against_oracle(got, x, b, K, G, TG, norm, scale, fn="none", mode=0, align=0):
+    E = x.shape[1]
+    xn, xcode = encode(x)
+    bn, bcode = encode(b)
+    oi, ow = oracle.router(xn, bn, K, G, TG, norm, scale, group_score=mode, scores_dtype=xcode,
+                           bias_dtype=None if b.dtype == torch.float32 else bcode,
+                           score_fn=FNS[fn][1])
+    assert np.array_equal(got["idx"], oi), \
+        "indices differ in %d tokens" % np.sum(np.any(got["idx"] != oi, 1))
+    if x.dtype == torch.float32:
+        assert_weights_close(got["w"], ow)
+    else:
+        assert_16bit_within_one_ulp(bf16_bits(got["w"]), ow, "router weights")
+    assert_indices_equal(got["ind"], oracle.create_indices(oi, E))
+    if align:
+        assert np.array_equal(got["scales"], oracle.scale_offsets(oi, E, align))
+
+
+def check_same(a, b_):
+    assert np.array_equal(a["idx"], b_["idx"])
+    wa = a["w"] if isinstance(a["w"], np.ndarray) else bf16_bits(a["w"])
+    wb = b_["w"] if isinstance(b_["w"], np.ndarray) else bf16_bits(b_["w"])
+    assert np.array_equal(np.asarray(wa).view(np.uint8), np.asarray(wb).view(np.uint8))
+    assert_indices_equal(a["ind"], b_["ind"])
+    if a["scales"] is not None:
+        assert np.array_equal(a["scales"], b_["scales"])
+
+
+@pytest.mark.parametrize("name,T", [("decode", 128), ("tiny", 64), ("mixtral", 2048),
+                                    ("dsv3", 2048), ("dsv3", 1), ("decode", 97)])
+@pytest.mark.parametrize("from_logits", [False, True])
+def test_workload_shapes(name, T, from_logits):
+    wk = wl.WORKLOADS[name].with_tokens(T)
+    log("route_and_index", wk.describe(), "logits" if from_logits else "scores")
+    b = wl.make_bias(wk)
+    if from_logits:
+        x, fn = wl.make_logits(wk), wk.score_fn
+    else:
+        x, fn = wl.make_scores(wk), "none"
+    args = (wk.K, wk.n_groups, wk.topk_group, wk.norm_weights, wk.scale, fn)
+    got = fused(x, b, *args)
+    check_against_oracle(got, x, b, *args)
+    check_same(got, separate(x, b, *args))
+
+
+@pytest.mark.parametrize("T,E,G,TG,K", [(1, 1, 1, 1, 1), (33, 2, 1, 1, 2), (129, 8, 4, 2, 3),
+                                        (300, 32, 8, 4, 6), (77, 64, 8, 3, 6),
+                                        (511, 128, 8, 4, 8), (1000, 256, 8, 4, 8),
+                                        (61, 512, 16, 4, 8), (2048, 1024, 16, 4, 8)])
+@pytest.mark.parametrize("levels", [0, 3])
+def test_random_shapes(T, E, G, TG, K, levels):
+    log("route_and_index random", T, E, G, TG, K, levels)
+    x = wl.random_scores(T, E, seed=T + E + levels, levels=levels)
+    b = wl.random_bias(E, seed=E + 5, std=0.02, levels=levels)
+    for norm, mode in ((True, 0), (False, 1)):
+        args = (K, G, TG, norm, 2.5, "none", mode)
+        got = fused(x, b, *args)
+        check_against_oracle(got, x, b, *args)
+        check_same(got, separate(x, b, *args))
+
+
+@pytest.mark.parametrize("sd,bd", [("bf16", "bf16"), ("bf16", "f32"), ("f16", "f16"),
+                                   ("f16", "f32")])
+@pytest.mark.parametrize("fn", ["none", "sigmoid", "softmax"])
+def test_16bit_inputs(sd, bd, fn):
+    T, E, G, TG, K = 300, 256, 8, 4, 8
+    log("route_and_index dtypes", sd, bd, fn)
+    g = torch.Generator().manual_seed(11)
+    if fn == "none":
+        x = wl.random_scores(T, E, seed=12, levels=5).to(DTYPES[sd])
+    else:
+        x = (torch.randn(T, E, generator=g) * 3).to(DTYPES[sd])
+    b = wl.random_bias(E, seed=13, std=0.02).to(DTYPES[bd])
+    args = (K, G, TG, True, 2.5, fn)
+    got = fused(x, b, *args)
+    check_against_oracle(got, x, b, *args)
+    check_same(got, separate(x, b, *args))
+
+
+@pytest.mark.parametrize("align", [1, 16, 128])
+def test_aligned_scale_offsets(align):
+    wk = wl.WORKLOADS["decode"]
+    log("route_and_index aligned", align)
+    x, b = wl.make_scores(wk), wl.make_bias(wk)
+    args = (wk.K, wk.n_groups, wk.topk_group, True, wk.scale, "none", 0, align)
+    got = fused(x, b, *args)
+    check_against_oracle(got, x, b, *args)
+    check_same(got, separate(x, b, *args))
+
+
+def test_empty_batch():
+    log("route_and_index T=0")
+    E, K = 256, 8
+    x = torch.zeros(0, E)
+    got = fused(x, torch.zeros(E), K, 8, 4, True, 1.0)
+    assert got["ind"]["expert_start_indices"].tolist() == [0] * (E + 1)
+    assert got["ind"]["expert_ids"].tolist() == [-1] * E
+    assert got["ind"]["expert_usage_stats"].tolist() == [0, 0]
+
+
+def test_back_to_back_calls_share_the_counter():
+    """Calls queued without synchronisation on one workspace, with sizes
+    going down and up: each must see the counter the previous one left."""
+    wk = wl.WORKLOADS["decode"]
+    log("route_and_index back to back")
+    ws = torch.zeros(1, dtype=torch.int32, device=DEV)
+    Ts = [128, 3, 2000, 17, 128, 1]
+    cases = []
+    for i, T in enumerate(Ts):
+        x = wl.random_scores(T, wk.E, seed=100 + i, levels=4 if i % 2 else 0)
+        b = wl.random_bias(wk.E, seed=7)
+        o = Outputs(T, wk.E, wk.K, torch.float32, False)
+        launch(o, x.to(DEV), b.to(DEV), ws, 8, 4, True, 2.5, binding.SCORE_NONE)
+        cases.append((x, b, o))
+    torch.cuda.synchronize()
+    assert int(ws.item()) == 0
+    for x, b, o in cases:
+        check_against_oracle(o.host(), x, b, wk.K, 8, 4, True, 2.5)
+
+
+def test_graph_replay():
+    """Captured once, replayed several times with eager work in between;
+    every replay gives the eager result and leaves the counter at zero."""
+    wk = wl.WORKLOADS["decode"]
+    log("route_and_index graph replay")
+    x = wl.make_scores(wk).to(DEV)
+    b = wl.make_bias(wk).to(DEV)
+    ws = torch.zeros(1, dtype=torch.int32, device=DEV)
+    eager = Outputs(wk.T, wk.E, wk.K, torch.float32, True)
+    launch(eager, x, b, ws, 8, 4, True, 2.5, binding.SCORE_NONE, align=16)
+    torch.cuda.synchronize()
+    ref = eager.host()
+    o = Outputs(wk.T, wk.E, wk.K, torch.float32, True)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        launch(o, x, b, ws, 8, 4, True, 2.5, binding.SCORE_NONE, align=16)  # warm-up
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launch(o, x, b, ws, 8, 4, True, 2.5, binding.SCORE_NONE, align=16,
+               stream=torch.cuda.current_stream())
+    for rep in range(4):
+        for t in (o.idx, o.order, o.restore, o.starts, o.eids, o.stats, o.scales):
+            t.fill_(POISON)
+        o.w.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(ws.item()) == 0, "replay %d left the counter set" % rep
+        check_same(o.host(), ref)
