@@ -27,6 +27,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -60,10 +61,16 @@ def parse():
 
 
 def finalize_source_hash() -> str:
+    """sha256 of the finalize kernel's sources with comments and layout
+    removed: any change to the code itself changes it, an edited comment
+    does not."""
     h = hashlib.sha256()
     for p in FINALIZE_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()
 
 

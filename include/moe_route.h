@@ -59,8 +59,8 @@ typedef enum {
  * computed in binary32 and rounded to nearest even on store. */
 
 /* How a group of experts is scored before the top-topk_group groups are
- * kept. The router page says only that the groups "with the highest scores"
- * survive; two readings are offered. */
+ * kept. The router page keeps the best-scoring groups without saying how a
+ * group's score is formed; two readings are offered. */
 typedef enum {
     MOE_GROUP_TOP2_SUM = 0, /* sum of the two largest biased scores in the group (default) */
     MOE_GROUP_MAX = 1       /* largest biased score in the group */
@@ -183,10 +183,11 @@ moe_status_t moe_create_indices(uint32_t* token_expert_order, uint32_t* expert_s
 
 /*
  * moe_create_indices_aligned
- * moe_create_indices plus the page's optional output scales_offset_p
- * ("aligned scale offsets for FP8/block-scaled grouped matmul"), padded as
- * the TokenFormat page's pad_expert_offsets pads offsets to the grouped
- * matmul's alignment. The pages name no alignment, so it is an argument.
+ * moe_create_indices plus the page's optional output scales_offset_p (Args:
+ * per-expert offsets of the scale rows that an FP8 / block-scaled grouped
+ * matmul reads, aligned), padded the way the TokenFormat page's
+ * pad_expert_offsets rounds offsets up to the grouped matmul's alignment.
+ * The pages name no alignment, so it is an argument.
  *
  *   scales_offset   out uint32 [E + 1], required: entry j = start of active
  *                   expert j's block of scale rows when every active expert's

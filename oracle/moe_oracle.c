@@ -181,8 +181,8 @@ static int keyed_desc(const void* a, const void* b) {
  *  1. biased score b[e] = score[e] + bias[e], one binary32 add; the bias is
  *     used for selection only.
  *  2. the E experts form n_groups consecutive groups of S = E / n_groups
- *     (E divisible by n_groups, Parameters: n_groups). The page says only
- *     that the topk_group groups "with the highest scores" survive; the
+ *     (E divisible by n_groups, Parameters: n_groups). The page keeps the
+ *     topk_group best-scoring groups without defining a group's score; the
  *     group score is, by reading, the sum of the two largest biased scores
  *     of the group (group_score = 0) or the single largest (group_score = 1).
  *     With S == 1 both are the single score.
@@ -376,7 +376,7 @@ int moe_oracle_create_indices(uint32_t* token_expert_order, uint32_t* expert_sta
 
 /*
  * Aligned scale offsets for a block-scaled grouped matmul (moe_create_indices
- * page, Args: scales_offset_p "aligned scale offsets"; TokenFormat page,
+ * page, Args: scales_offset_p, aligned offsets of the scale rows; TokenFormat page,
  * pad_expert_offsets: offsets padded to the grouped matmul's alignment).
  * The pages give no alignment, so it is an argument. By reading, entry j of
  * scales_offset [E + 1] is where active expert j's block of scale rows
@@ -413,7 +413,7 @@ int moe_oracle_scale_offsets(uint32_t* scales_offset, const int32_t* topk_ids, i
 /*
  * output[t, h] = sum over k = 0..K-1 of router_weight[t, k] *
  *                down[restore_order[t*K + k], h]
- * accumulated in binary32 (the page: "accumulates in fp32"), starting from
+ * accumulated in binary32 (the page keeps the sum in fp32), starting from
  * +0 and adding the K terms in k order, each term fused into the running
  * sum by one correctly rounded fmaf. The accumulator is then stored as
  * out_type (bf16 and fp16 by round to nearest even). down, router_weight

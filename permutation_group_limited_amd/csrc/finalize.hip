@@ -1,9 +1,9 @@
 // Fused unpermute gather + weighted top-k sum for gfx950.
 //
 // Computes what the moe_finalize page (Modular MAX Mojo API, nn/moe)
-// describes: each output row gathers its token's K rows of `down` through
-// restore_order, scales each by its router weight and accumulates in fp32;
-// the [T, K, H] unpermuted tensor is never formed.
+// describes: output row t is the sum over k of router weight (t, k) times
+// the row of `down` that restore_order names for slot t*K + k, with the sum
+// held in fp32; the [T, K, H] unpermuted tensor is never formed.
 //
 // HBM-bound streaming gather. Mapping: one wave64 per (token, 64 x 16-byte
 // column chunk of the row). The wave's token is uniform, so its K restore
