@@ -224,7 +224,10 @@ moe_status_t moe_finalize(void* output, moe_dtype_t out_dtype, const void* down,
   if (!dtype_ok(out_dtype) || !dtype_ok(down_dtype) || !dtype_ok(weight_dtype))
     return MOE_ERR_INVALID_ARG;
   if (T > (int64_t)UINT32_MAX / K) return MOE_ERR_INVALID_ARG;
-  if (H > ((int64_t)1 << 40)) return MOE_ERR_INVALID_ARG;
+  // an output row must stay below 2^31 bytes (its stores address it in 32 bits)
+  if (H > (int64_t)INT32_MAX ||
+      H * static_cast<int64_t>(dtype_bytes(out_dtype)) > (int64_t)INT32_MAX - 16)
+    return MOE_ERR_UNSUPPORTED;
   if (T > 0 && H > 0 && (!output || !down || !restore_order || !router_weight))
     return MOE_ERR_INVALID_ARG;
   if ((H * static_cast<int64_t>(dtype_bytes(down_dtype))) % 16 != 0) return MOE_ERR_ALIGNMENT;

@@ -11,9 +11,8 @@
 // K independent 16-byte non-temporal loads (one per gathered row, all in
 // flight together; every row segment is read exactly once), folds them with
 // one fmaf per element in ascending k, and writes its output slice with one
-// ordinary store (measured a little faster than a non-temporal store here).
-// Rows are addressed in 64 bits (T*K*H elements exceed 2^32 for large
-// prefill batches).
+// 16-byte buffer store (cache policy below). Rows of `down` are addressed in
+// 64 bits (T*K*H elements exceed 2^32 for large prefill batches).
 #include "common.hpp"
 
 namespace moe {
@@ -36,10 +35,18 @@ __device__ __forceinline__ void widen16(const u32x4& v, float* f) {
   }
 }
 
-// Store VEC fp32 accumulators as D at p (VEC * kBytes bytes, one or two
-// vector stores).
+// Output stores go through a buffer resource spanning the token's output
+// row, with cache policy sc1: on the DSv3-shaped gather that ran 3-4% faster
+// than default or non-temporal stores (measured; the loads stay
+// non-temporal, which matters far more).
+constexpr int kStorePolicy = 16;         // cache-policy operand: sc1
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
+
+// Store VEC fp32 accumulators as D at byte offset `off` of the row (VEC *
+// kBytes bytes, one or two vector stores).
 template <typename D, int VEC>
-__device__ __forceinline__ void store_out(typename D::storage* p, const float* acc) {
+__device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t row, uint32_t off,
+                                          const float* acc) {
   if constexpr (D::kBytes == 4) {
 #pragma unroll
     for (int q = 0; q < VEC; q += 4) {
@@ -48,7 +55,8 @@ __device__ __forceinline__ void store_out(typename D::storage* p, const float* a
       v.y = D::narrow_bits(acc[q + 1]);
       v.z = D::narrow_bits(acc[q + 2]);
       v.w = D::narrow_bits(acc[q + 3]);
-      *reinterpret_cast<u32x4*>(p + q) = v;
+      __builtin_amdgcn_raw_buffer_store_b128(v, row, static_cast<int>(off + q * 4), 0,
+                                             kStorePolicy);
     }
   } else if constexpr (VEC == 8) {
     u32x4 v;
@@ -56,12 +64,12 @@ __device__ __forceinline__ void store_out(typename D::storage* p, const float* a
     v.y = D::narrow_bits(acc[2]) | (D::narrow_bits(acc[3]) << 16);
     v.z = D::narrow_bits(acc[4]) | (D::narrow_bits(acc[5]) << 16);
     v.w = D::narrow_bits(acc[6]) | (D::narrow_bits(acc[7]) << 16);
-    *reinterpret_cast<u32x4*>(p) = v;
+    __builtin_amdgcn_raw_buffer_store_b128(v, row, static_cast<int>(off), 0, kStorePolicy);
   } else {
     u32x2 v;
     v.x = D::narrow_bits(acc[0]) | (D::narrow_bits(acc[1]) << 16);
     v.y = D::narrow_bits(acc[2]) | (D::narrow_bits(acc[3]) << 16);
-    *reinterpret_cast<u32x2*>(p) = v;
+    __builtin_amdgcn_raw_buffer_store_b64(v, row, static_cast<int>(off), 0, kStorePolicy);
   }
 }
 
@@ -128,7 +136,11 @@ __global__ __launch_bounds__(kBlock) void finalize_kernel(
       for (int e = 0; e < VEC; ++e) acc[e] = fmaf(wj, d[e], acc[e]);
     }
   }
-  store_out<DO, VEC>(out + t * H + h, acc);
+  // the host keeps a row below 2^31 bytes, so offsets fit the resource
+  constexpr int64_t kOutBytes = sizeof(typename DO::storage);
+  const __amdgpu_buffer_rsrc_t row = __builtin_amdgcn_make_buffer_rsrc(
+      out + t * H, 0, static_cast<int>(H * kOutBytes), kRsrcWord3);
+  store_out<DO, VEC>(row, static_cast<uint32_t>(h * kOutBytes), acc);
 }
 
 template <typename DD, typename DO>

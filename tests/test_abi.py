@@ -115,6 +115,9 @@ def finalize(lib, T=4, K=2, H=64, od=1, dd=1, wd=0, ptrs=None):
     (dict(ptrs=(FAKE_MIS, FAKE, FAKE, FAKE)), ALIGNMENT),
     (dict(ptrs=(FAKE, FAKE, FAKE, None)), INVALID),
     (dict(T=0, ptrs=(None,) * 4), OK), (dict(H=0, ptrs=(None,) * 4), OK),
+    # output rows of 2^31 bytes or more are not supported
+    (dict(H=1 << 29, od=0), UNSUPPORTED), (dict(H=1 << 30, od=1), UNSUPPORTED),
+    (dict(H=1 << 40), UNSUPPORTED),
 ])
 def test_finalize_validation(lib, kw, code):
     assert finalize(lib, **kw) == code
