@@ -95,8 +95,9 @@ typedef enum {
  * Validation: T >= 0; E >= 1 and E % n_groups == 0; 1 <= topk_group <=
  * n_groups <= 64; 1 <= K <= topk_group * S; K <= 64; non-NULL pointers when
  * T > 0; expert_scores and expert_bias 16-byte aligned. Supported: scores
- * F32, BF16 or F16 with bias of the same dtype or F32; E a power of two,
- * 1 <= E <= 1024 (other E give MOE_ERR_UNSUPPORTED).
+ * F32, BF16 or F16 with bias of the same dtype or F32; 1 <= E <= 1024
+ * (larger E give MOE_ERR_UNSUPPORTED). Powers of two take the fastest
+ * form; other E run one token per wave with the group stage in LDS.
  */
 moe_status_t moe_router_group_limited(int32_t* expert_indices, void* expert_weights,
                                       const void* expert_scores, const void* expert_bias,
@@ -242,9 +243,9 @@ size_t moe_route_and_index_workspace_size(void);
  *                    must not run concurrently (one stream, or ordered
  *                    streams).
  *
- * Validation: that of the two separate calls, plus T * K <= 16384 (larger
- * batches give MOE_ERR_UNSUPPORTED: the index step runs on one workgroup,
- * and the separate calls are faster there). With T = 0 only the index
+ * Validation: that of the two separate calls, plus T * K <= 16384 and E
+ * a power of two (otherwise MOE_ERR_UNSUPPORTED: the index step runs on
+ * one workgroup, and the separate calls serve the rest). With T = 0 only the index
  * metadata outputs are written, as moe_create_indices does for N = 0.
  */
 moe_status_t moe_route_and_index(int32_t* expert_indices, void* expert_weights,

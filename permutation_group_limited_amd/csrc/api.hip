@@ -54,7 +54,7 @@ static moe_status_t router_check(int32_t* expert_indices, void* expert_weights,
     return MOE_ERR_INVALID_ARG;
   if (T > (int64_t)UINT32_MAX / K) return MOE_ERR_INVALID_ARG;
   if (!router_dtypes_supported(scores_dtype, bias_dtype)) return MOE_ERR_UNSUPPORTED;
-  if (!is_pow2(E) || E > 1024) return MOE_ERR_UNSUPPORTED;
+  if (E > 1024) return MOE_ERR_UNSUPPORTED;
   if (!aligned(expert_scores, 16) || !aligned(expert_bias, 16) || !aligned(expert_indices, 4) ||
       !aligned(expert_weights, dtype_bytes(scores_dtype)))
     return MOE_ERR_ALIGNMENT;
@@ -201,7 +201,7 @@ moe_status_t moe_route_and_index(int32_t* expert_indices, void* expert_weights,
   if (st != MOE_OK) return st;
   if (workspace == nullptr || workspace_bytes < sizeof(uint32_t)) return MOE_ERR_WORKSPACE;
   if (!aligned(workspace, 4)) return MOE_ERR_ALIGNMENT;
-  if (N > kRouteIndexMaxSlots) return MOE_ERR_UNSUPPORTED;
+  if (N > kRouteIndexMaxSlots || !is_pow2(E)) return MOE_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (T == 0)  // nothing to route: the index step alone writes the metadata
     return launch_indices(token_expert_order, expert_start_indices, restore_token_order,

@@ -9,7 +9,10 @@
 // used): a token is owned by LPT consecutive lanes of a wave64, each lane
 // holding EPL consecutive experts (E = LPT * EPL). For E >= 64 a token fills
 // a whole wave (E = 256: 4 experts, one 16-byte load per lane); for E < 64
-// several tokens share a wave.
+// several tokens share a wave. E that is not a power of two takes a general
+// form (router_any_e_kernel): one wave per token with EPL * 64 >= E, absent
+// experts never candidates, and the group stage below replaced by a scan of
+// each group's scores staged in LDS.
 //
 //  * group score: lane-local top-2, then a top-2 merge over the LPG = S/EPL
 //    lanes of a group through DPP (quad_perm, row_half_mirror, row_mirror),
@@ -53,14 +56,53 @@ struct RouterLaunch {
   }
 };
 
+// Any E up to 1024 (not a power of two): one wave per token, EPL experts
+// per lane with EPL * 64 >= E, group stage through LDS.
+template <typename DS, typename DB, int EPL, int FN>
+__global__ __launch_bounds__(kBlock) void router_any_e_kernel(
+    int32_t* __restrict__ out_idx, typename DS::storage* __restrict__ out_w,
+    const typename DS::storage* __restrict__ scores, const typename DB::storage* __restrict__ bias,
+    int64_t T, int32_t K, int32_t n_groups, int32_t topk_group, int32_t norm_weights,
+    float scale, int32_t mode, int32_t E) {
+  route_tokens<DS, DB, EPL, kWave, FN, kWavesPerBlock, true>(
+      out_idx, out_w, scores, bias, T, K, n_groups, topk_group, norm_weights, scale, mode, E);
+}
+
+// Reached through dispatch_router with the padded expert count
+// max(64, next power of two >= E), so LPT is always a full wave here.
+template <typename DS, typename DB, int EPL, int LPT, int FN>
+struct RouterAnyELaunch {
+  static moe_status_t run(int32_t* idx, void* w, const void* s, const void* b, int64_t T,
+                          int32_t K, int32_t G, int32_t TG, int32_t norm, float scale,
+                          int32_t mode, int32_t E, hipStream_t stream) {
+    if constexpr (LPT != kWave) {
+      return MOE_ERR_UNSUPPORTED;
+    } else {
+      const int64_t blocks = (T + kWavesPerBlock - 1) / kWavesPerBlock;
+      hipLaunchKernelGGL((router_any_e_kernel<DS, DB, EPL, FN>),
+                         dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, stream, idx,
+                         static_cast<typename DS::storage*>(w),
+                         static_cast<const typename DS::storage*>(s),
+                         static_cast<const typename DB::storage*>(b), T, K, G, TG, norm, scale,
+                         mode, E);
+      return check_launch();
+    }
+  }
+};
+
 }  // namespace
 
 moe_status_t launch_router(int32_t* idx, void* w, const void* s, const void* b,
                            moe_dtype_t sd, moe_dtype_t bd, int32_t fn, int64_t T, int32_t E,
                            int32_t K, int32_t G, int32_t TG, int32_t norm, float scale,
                            int32_t mode, hipStream_t stream) {
-  return dispatch_router<RouterLaunch>(sd, bd, fn, E, idx, w, s, b, T, K, G, TG, norm, scale,
-                                       mode, stream);
+  if ((E & (E - 1)) == 0)
+    return dispatch_router<RouterLaunch>(sd, bd, fn, E, idx, w, s, b, T, K, G, TG, norm, scale,
+                                         mode, stream);
+  int32_t padded = kWave;
+  while (padded < E) padded <<= 1;
+  return dispatch_router<RouterAnyELaunch>(sd, bd, fn, padded, idx, w, s, b, T, K, G, TG, norm,
+                                           scale, mode, E, stream);
 }
 
 }  // namespace moe

@@ -170,13 +170,21 @@ __device__ __forceinline__ double segment_sum_f64(double v) {
 
 // Routes the tokens of workgroup blockIdx.x (WPB waves of kWave / LPT
 // tokens each) and writes their expert_indices and expert_weights rows.
-template <typename DS, typename DB, int EPL, int LPT, int FN, int WPB>
+//
+// GEN = false: E = EPL * LPT, a power of two, and groups of S = E / n_groups
+// experts cover whole lanes (S >= EPL), so the group stage is a lane
+// butterfly. GEN = true: any E_rt <= EPL * 64 (one wave per token, LPT =
+// 64); lane l holds experts [l * EPL, l * EPL + EPL) of which those >= E_rt
+// are absent, and the group stage goes through LDS: the biased scores are
+// staged per wave, lane g scans group g, and the kept groups form a mask.
+template <typename DS, typename DB, int EPL, int LPT, int FN, int WPB, bool GEN = false>
 __device__ __forceinline__ void route_tokens(
     int32_t* __restrict__ out_idx, typename DS::storage* __restrict__ out_w,
     const typename DS::storage* __restrict__ scores, const typename DB::storage* __restrict__ bias,
     int64_t T, int32_t K, int32_t n_groups, int32_t topk_group, int32_t norm_weights,
-    float scale, int32_t mode) {
-  constexpr int E = EPL * LPT;
+    float scale, int32_t mode, int32_t E_rt = 0) {
+  static_assert(!GEN || LPT == kWave, "the general-E form routes one token per wave");
+  const int32_t E = GEN ? E_rt : EPL * LPT;
   constexpr int TPW = kWave / LPT;  // tokens per wave
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
@@ -190,13 +198,25 @@ __device__ __forceinline__ void route_tokens(
       (LPT == kWave) ? ~0ull : (((1ull << LPT) - 1ull) << tok_lane0);
 
   float s[EPL], bi[EPL], b[EPL];
-  if (tok_ok) {
-    load_row<DS, EPL>(s, scores + t * E + e0);
-  } else {
+  bool present[EPL];  // expert e0 + i exists (always, unless GEN)
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) s[i] = 0.0f;
+  for (int i = 0; i < EPL; ++i) present[i] = !GEN || e0 + i < E;
+  if constexpr (GEN) {
+    // rows of E elements need not be 16-byte multiples: element loads
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      s[i] = (tok_ok && present[i]) ? load_f32<DS>(scores, t * E + e0 + i) : 0.0f;
+      bi[i] = present[i] ? load_f32<DB>(bias, e0 + i) : 0.0f;
+    }
+  } else {
+    if (tok_ok) {
+      load_row<DS, EPL>(s, scores + t * E + e0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) s[i] = 0.0f;
+    }
+    load_row<DB, EPL>(bi, bias + e0);
   }
-  load_row<DB, EPL>(bi, bias + e0);
   // scores from logits (FN != kScoreLoad)
   double sm_max = 0.0, sm_sum = 1.0;
   if constexpr (FN == kScoreSigmoid) {
@@ -205,12 +225,12 @@ __device__ __forceinline__ void route_tokens(
   } else if constexpr (FN == kScoreSoftmax) {
     uint32_t km = 0;
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) km = umax(km, ordered_key(s[i]));
+    for (int i = 0; i < EPL; ++i) km = present[i] ? umax(km, ordered_key(s[i])) : km;
     sm_max = static_cast<double>(key_to_float(segment_max<LPT>(km)));
     double ex[EPL], part = 0.0;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-      ex[i] = exp(static_cast<double>(s[i]) - sm_max);
+      ex[i] = present[i] ? exp(static_cast<double>(s[i]) - sm_max) : 0.0;
       part += ex[i];
     }
     sm_sum = segment_sum_f64<LPT>(part);
@@ -221,8 +241,49 @@ __device__ __forceinline__ void route_tokens(
   for (int i = 0; i < EPL; ++i) b[i] = s[i] + bi[i];
 
   // ---- group stage: keep the best topk_group groups ------------------------
-  bool kept = true;
-  if (topk_group < n_groups) {
+  bool kept[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) kept[i] = true;
+  if constexpr (GEN) {
+    if (topk_group < n_groups) {
+      // Stage the token's biased scores in this wave's LDS row; LDS
+      // operations of one wave take effect in order, so its lanes may read
+      // each other's stores after a wave-level scheduling barrier.
+      __shared__ float staged[WPB][EPL * kWave];
+      float* row = staged[wave];
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (present[i]) row[e0 + i] = b[i];
+      __builtin_amdgcn_wave_barrier();
+      const int S = E / n_groups;
+      float gs = -__builtin_inff();
+      if (lane < n_groups) {
+        float m1 = -__builtin_inff(), m2 = -__builtin_inff();
+        for (int j = lane * S; j < lane * S + S; ++j) {
+          const float v = row[j];
+          m2 = fmaxf(m2, fminf(m1, v));
+          m1 = fmaxf(m1, v);
+        }
+        gs = (mode == MOE_GROUP_MAX || S == 1) ? m1 : m1 + m2;
+      }
+      // rank of group `lane` = groups that beat it (ties: lower index)
+      int beats = 0;
+      for (int j = 0; j < n_groups; ++j) {
+        const float o = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gs), j));
+        beats += (o > gs) || (o == gs && j < lane);
+      }
+      const uint64_t keep = __ballot(lane < n_groups && beats < topk_group);
+      // group of expert e = floor((e + 1/2) / S), exact in binary32 for
+      // e, S < 2^10: the quotient stays at least 1/(2S) from an integer
+      const float inv_s = 1.0f / static_cast<float>(S);
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const int g = static_cast<int>((static_cast<float>(e0 + i) + 0.5f) * inv_s);
+        kept[i] = present[i] && ((keep >> (g & 63)) & 1ull) != 0;
+      }
+    }
+  } else if (topk_group < n_groups) {
     // E, n_groups and EPL are powers of two: shifts, not divisions
     const int lg_groups = __builtin_ctz(static_cast<uint32_t>(n_groups));
     const int S = E >> lg_groups;
@@ -245,7 +306,9 @@ __device__ __forceinline__ void route_tokens(
       const float o = __shfl(gs, tok_lane0 + j * LPG, kWave);
       beats += (o > gs) || (o == gs && j < my_g);
     }
-    kept = group_sum(beats, LPG) < topk_group;
+    const bool k_lane = group_sum(beats, LPG) < topk_group;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) kept[i] = k_lane;
   }
 
   // ---- top-K: K rounds of segment max over the lanes' sorted heads ---------
@@ -259,7 +322,7 @@ __device__ __forceinline__ void route_tokens(
   uint32_t ki[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
-    kv[i] = (tok_ok && kept) ? ordered_key(b[i]) : 0u;
+    kv[i] = (tok_ok && kept[i] && present[i]) ? ordered_key(b[i]) : 0u;
     ki[i] = static_cast<uint32_t>(i);
   }
   sort_desc<EPL>(kv, ki);

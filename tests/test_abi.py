@@ -66,7 +66,9 @@ def router(lib, T=4, E=256, K=8, G=8, TG=4, norm=1, mode=0, ptrs=None, sd=0, bd=
     (dict(K=0), INVALID), (dict(K=129, TG=4), INVALID), (dict(E=256, G=8, TG=1, K=33), INVALID),
     (dict(E=1024, G=1, TG=1, K=65), INVALID), (dict(mode=2), INVALID), (dict(sd=7), INVALID),
     (dict(sd=1, bd=2), UNSUPPORTED), (dict(bd=1), UNSUPPORTED), (dict(sd=2, bd=1), UNSUPPORTED),
-    (dict(E=96, G=8, TG=4), UNSUPPORTED),
+    # any E up to 1024 is supported (T = 0: validated, nothing launched)
+    (dict(E=96, G=8, TG=4, T=0), OK), (dict(E=1000, G=8, TG=4, T=0), OK),
+    (dict(E=160, G=8, TG=3, K=6, ptrs=(FAKE, FAKE, FAKE_MIS, FAKE)), ALIGNMENT),
     (dict(E=2048, G=8, TG=4), UNSUPPORTED),
     (dict(ptrs=(None, FAKE, FAKE, FAKE)), INVALID),
     (dict(ptrs=(FAKE, FAKE, FAKE_MIS, FAKE)), ALIGNMENT),
