@@ -14,12 +14,22 @@
 namespace moe {
 
 constexpr int kWave = 64;
-constexpr int kBlock = 256;  // 4 waves per workgroup for every kernel
+constexpr int kBlock = 256;  // workgroup of the router and finalize kernels (4 waves)
 constexpr int kWavesPerBlock = kBlock / kWave;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// DPP controls (gfx9 encoding) used by the cross-lane steps: shift right by
+// n lanes inside each row of 16, and broadcast of lane 15 of a row into the
+// next row / of lane 31 into rows 2 and 3.
+constexpr int kRowShr1 = 0x111;
+constexpr int kRowShr2 = 0x112;
+constexpr int kRowShr4 = 0x114;
+constexpr int kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142;
+constexpr int kRowBcast31 = 0x143;
 
 // ---- element types -------------------------------------------------------
 // Storage tags for the three dtypes of the ABI. Widening to fp32 is exact;

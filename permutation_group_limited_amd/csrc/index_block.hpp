@@ -17,15 +17,6 @@ __device__ __forceinline__ int key_bits(int E) {
   return nb;
 }
 
-// DPP controls (gfx9 encoding): shift right by n lanes inside each row of
-// 16, and broadcast of lane 15 / lane 31 into the following row(s).
-constexpr int kRowShr1 = 0x111;
-constexpr int kRowShr2 = 0x112;
-constexpr int kRowShr4 = 0x114;
-constexpr int kRowShr8 = 0x118;
-constexpr int kRowBcast15 = 0x142;
-constexpr int kRowBcast31 = 0x143;
-
 // Value of `x` from the lane the DPP control names; 0 where the row / bank
 // mask leaves a lane out or the source lies outside the row.
 template <int CTRL, int ROWS>

@@ -106,7 +106,9 @@ __device__ __forceinline__ int group_sum(int x, int lpg) {
 // Maximum of v over the token's LPT lanes, returned to every lane of the
 // segment: xor 1 and xor 2 inside quads, mirrored half-rows and rows (by
 // then each quad, resp. half-row, is uniform), xor 16 by ds_swizzle; for a
-// full wave the four row maxima are combined through v_readlane.
+// full wave, the row maxima are carried across rows by the row_bcast:15 and
+// row_bcast:31 moves (lane 63 ends with the wave maximum) and read back
+// with one v_readlane.
 template <int LPT>
 __device__ __forceinline__ uint32_t segment_max(uint32_t v) {
   if (LPT >= 2) v = umax(v, dpp_u<kXor1>(v));
@@ -116,31 +118,34 @@ __device__ __forceinline__ uint32_t segment_max(uint32_t v) {
   if constexpr (LPT == 32) {
     v = umax(v, static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), 0x401F)));
   } else if constexpr (LPT == kWave) {
-    const int x = static_cast<int>(v);
-    v = umax(umax(static_cast<uint32_t>(__builtin_amdgcn_readlane(x, 0)),
-                  static_cast<uint32_t>(__builtin_amdgcn_readlane(x, 16))),
-             umax(static_cast<uint32_t>(__builtin_amdgcn_readlane(x, 32)),
-                  static_cast<uint32_t>(__builtin_amdgcn_readlane(x, 48))));
+    // rows outside the row mask take 0, the identity of the maximum
+    v = umax(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v),
+                                                                  kRowBcast15, 0xA, 0xF, false)));
+    v = umax(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v),
+                                                                  kRowBcast31, 0xC, 0xF, false)));
+    v = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), kWave - 1));
   }
   return v;
 }
 
-// Stable descending sort of keys held in registers, carrying each key's
-// element index along: adjacent exchanges that swap only on a strictly
-// larger key keep equal keys in ascending element order.
+// Descending bitonic sorting network over EPL (a power of two) distinct
+// 64-bit values, unrolled at compile time.
 template <int EPL>
-__device__ __forceinline__ void sort_desc(uint32_t (&k)[EPL], uint32_t (&e)[EPL]) {
+__device__ __forceinline__ void sort_desc_u64(uint64_t (&p)[EPL]) {
 #pragma unroll
-  for (int i = 1; i < EPL; ++i) {
+  for (int k = 2; k <= EPL; k <<= 1) {
 #pragma unroll
-    for (int j = i; j > 0; --j) {
-      const bool sw = k[j] > k[j - 1];
-      const uint32_t k0 = sw ? k[j] : k[j - 1], k1 = sw ? k[j - 1] : k[j];
-      const uint32_t e0 = sw ? e[j] : e[j - 1], e1 = sw ? e[j - 1] : e[j];
-      k[j - 1] = k0;
-      k[j] = k1;
-      e[j - 1] = e0;
-      e[j] = e1;
+    for (int j = k >> 1; j > 0; j >>= 1) {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const int l = i ^ j;
+        if (l > i) {
+          const uint64_t a = p[i], b = p[l];
+          const bool sw = ((i & k) == 0) ? (a < b) : (a > b);
+          p[i] = sw ? b : a;
+          p[l] = sw ? a : b;
+        }
+      }
     }
   }
 }
@@ -313,52 +318,55 @@ __device__ __forceinline__ void route_tokens(
 
   // ---- top-K: K rounds of segment max over the lanes' sorted heads ---------
   // Keys preserve the order of the biased scores (0 = not a candidate). Each
-  // lane sorts its EPL (key, element) pairs by key desc, element asc. A
-  // round takes the segment maximum of the lane heads; among lanes whose
-  // head equals it the lowest lane wins, which is the lowest expert id
-  // because lanes hold ascending, disjoint id ranges. The winner pops its
-  // head. Round k yields slot k.
-  uint32_t kv[EPL];
-  uint32_t ki[EPL];
+  // lane sorts its EPL elements by (key desc, element asc), packed as
+  // key << 32 | (EPL - 1 - element) so that all packed values of a lane are
+  // distinct. A round takes the segment maximum of the lane heads' keys;
+  // among lanes whose head key equals it the lowest lane wins, which is the
+  // lowest expert id because lanes hold ascending, disjoint id ranges. The
+  // winner pops its head. Round k yields slot k.
+  uint64_t pk[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
-    kv[i] = (tok_ok && kept[i] && present[i]) ? ordered_key(b[i]) : 0u;
-    ki[i] = static_cast<uint32_t>(i);
+    const uint32_t key = (tok_ok && kept[i] && present[i]) ? ordered_key(b[i]) : 0u;
+    pk[i] = (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(EPL - 1 - i);
   }
-  sort_desc<EPL>(kv, ki);
+  sort_desc_u64<EPL>(pk);
 
   uint32_t my_id = 0;
   for (int k = 0; k < K; ++k) {
-    const uint32_t head = kv[0];
+    const uint32_t head = static_cast<uint32_t>(pk[0] >> 32);
     const uint64_t bal = __ballot(head == segment_max<LPT>(head)) & segmask;
     const int win = __builtin_ctzll(static_cast<unsigned long long>(bal));
     uint32_t id;
     if constexpr (LPT == kWave) {
-      id = static_cast<uint32_t>(win * EPL) +
-           static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ki[0]), win));
+      const uint32_t low = static_cast<uint32_t>(
+          __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(pk[0])), win));
+      id = static_cast<uint32_t>(win * EPL + (EPL - 1)) - (low & (EPL - 1));
     } else {
       id = static_cast<uint32_t>(win - tok_lane0);  // one expert per lane
     }
     if (sub == k) my_id = id;
     if (lane == win) {
 #pragma unroll
-      for (int i = 0; i + 1 < EPL; ++i) {
-        kv[i] = kv[i + 1];
-        ki[i] = ki[i + 1];
-      }
-      kv[EPL - 1] = 0u;
+      for (int i = 0; i + 1 < EPL; ++i) pk[i] = pk[i + 1];
+      pk[EPL - 1] = 0u;
     }
   }
 
   // ---- weights from the unbiased scores -----------------------------------
+  // Slot `sub`'s score is still in the registers of the lane that holds
+  // its expert: fetch it across lanes (one ds_bpermute per element
+  // register) instead of reading the row again.
   const bool slot = tok_ok && sub < K;
   if (my_id >= static_cast<uint32_t>(E)) my_id = 0;  // unreachable with finite scores
+  const int owner = (LPT == kWave) ? static_cast<int>(my_id / EPL)
+                                   : tok_lane0 + static_cast<int>(my_id);
+  const int elem = static_cast<int>(my_id % EPL);
   float u = 0.0f;
-  if (slot) {
-    u = load_f32<DS>(scores, t * E + my_id);
-    if constexpr (FN == kScoreSigmoid) u = sigmoid_f64(u);
-    if constexpr (FN == kScoreSoftmax)
-      u = static_cast<float>(exp(static_cast<double>(u) - sm_max) / sm_sum);
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const float v = __shfl(s[i], owner, kWave);
+    u = (i == elem) ? v : u;
   }
   float w;
   if (norm_weights) {
