@@ -2,18 +2,21 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3]
 
-One step = one pass of the whole path over one batch: router ->
-create_indices -> finalize, all through the C ABI on torch's current
-stream, with every input already resident in HBM. W untimed steps, then K
-timed steps between a synchronize and HIP events; prints ONE JSON line.
+One step = one pass of the whole path over one batch: router and index
+creation through moe_route_and_index (two kernels: the router, which also
+fills the index step's per-chunk histogram, then the scatter), then
+moe_finalize, all through the C ABI on torch's current stream, with every
+input already resident in HBM. W untimed steps, then K timed steps between
+a synchronize and HIP events; prints ONE JSON line.
 
 Headline workload: DeepSeek-V3-shaped, T=8192 tokens, E=256 experts in 8
 groups (4 kept), K=8, hidden 7168, bf16 expert outputs and output. One
 routed token-slot is one (token, k) pair, i.e. one row of `down`.
 
 Reported beside the throughput:
-  * per-stage mean durations: each stage K times back to back on the launch
-    stream between two HIP events;
+  * per-stage mean durations: each entry point (router, create_indices,
+    route_and_index, finalize) K times back to back on the launch stream
+    between two HIP events;
   * roofline of the dominant kernel (finalize): algorithmic bytes per launch
     (T*K*H*2 read + T*K*(4+4) restore and weights + T*H*2 written) divided by
     its mean duration above, against 8 TB/s; plus the HBM bytes measured by
@@ -122,6 +125,9 @@ def main():
     stats = torch.empty(2, dtype=torch.int32, device=dev)
     ws = torch.empty(max(binding.moe_create_indices_workspace_size(N, E), 4) // 4,
                      dtype=torch.int32, device=dev)
+    # moe_route_and_index's workspace: zero once here, left zero by every call
+    ws_ri = torch.zeros(binding.moe_route_and_index_workspace_size(T, K, E) // 4,
+                        dtype=torch.int32, device=dev)
     out = torch.empty(T, H, dtype=wk.out_dtype, device=dev)
 
     def router():
@@ -131,12 +137,18 @@ def main():
     def indices():
         binding.moe_create_indices(order, starts, restore, eids, stats, idx, ws)
 
+    def route_and_index():
+        binding.moe_route_and_index(idx, wts, order, starts, restore, eids, stats, scores, bias,
+                                    ws_ri, wk.n_groups, wk.topk_group, wk.norm_weights, wk.scale)
+
     def finalize():
         binding.moe_finalize(out, down, restore, wts)
 
+    # One step = the whole path on one batch: router and index creation
+    # through moe_route_and_index (the router also fills the index step's
+    # histogram), then finalize. The separate entry points are timed below.
     def step():
-        router()
-        indices()
+        route_and_index()
         finalize()
 
     for _ in range(args.warmup):
@@ -160,7 +172,7 @@ def main():
     # timed region 2: each stage K times back to back on the launch stream
     # (every stage is idempotent on its inputs), bracketed by events, for
     # per-stage mean durations; finalize's is the roofline's denominator
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
     torch.cuda.synchronize()
     ev[0].record()
     for _ in range(args.steps):
@@ -170,11 +182,15 @@ def main():
         indices()
     ev[2].record()
     for _ in range(args.steps):
-        finalize()
+        route_and_index()
     ev[3].record()
+    for _ in range(args.steps):
+        finalize()
+    ev[4].record()
     torch.cuda.synchronize()
     stage_ms = {name: ev[j].elapsed_time(ev[j + 1]) / args.steps
-                for j, name in enumerate(("router", "create_indices", "finalize"))}
+                for j, name in enumerate(("router", "create_indices", "route_and_index",
+                                          "finalize"))}
     fin_avg_ms = stage_ms["finalize"]
 
     bytes_router = T * E * 4 + E * 4 + N * (4 + 4)
@@ -206,6 +222,8 @@ def main():
         "algorithmic_bytes_per_step": bytes_total,
         "stage_bytes": {"router": bytes_router, "create_indices": bytes_indices,
                         "finalize": bytes_finalize},
+        "step": "moe_route_and_index (router filling the index histogram, then the scatter) "
+                "+ moe_finalize: 3 kernels",
         "stage_ms": stage_ms,
         "wall_s": wall,
         "roofline": {"kernel": "finalize_kernel", "bound": "hbm", "achieved": fin_gbps,
@@ -264,6 +282,9 @@ def extras(wk, scores_h, bias_h, idx, wts, steps):
     """Side measurements of the widened entry points:
       * the router on logits (sigmoid computed in the kernel) against the
         router on precomputed scores, same workload, K back-to-back launches;
+      * router + index creation through the two entry points against
+        moe_route_and_index (router filling the index histogram), same
+        workload;
       * the decode-shaped workload (T=128): whole steps (router ->
         create_indices -> finalize) captured 20 to a HIP graph, mean GPU time
         per step (eager launches would measure the host, not the GPU); the
@@ -299,6 +320,27 @@ def extras(wk, scores_h, bias_h, idx, wts, steps):
     res["router_scores_ms"] = run(lambda: binding.moe_router_group_limited(
         idx, wts, scores, bias, wk.n_groups, wk.topk_group, wk.norm_weights, wk.scale))
 
+    # router + index creation: two entry points vs moe_route_and_index
+    T, E, K = wk.T, wk.E, wk.K
+    o1, r1 = (torch.empty(T * K, dtype=torch.int32, device=dev) for _ in range(2))
+    st1 = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    e1 = torch.empty(E, dtype=torch.int32, device=dev)
+    u1 = torch.empty(2, dtype=torch.int32, device=dev)
+    ws1 = torch.empty(max(binding.moe_create_indices_workspace_size(T * K, E), 4) // 4,
+                      dtype=torch.int32, device=dev)
+    tk1 = torch.zeros(binding.moe_route_and_index_workspace_size(T, K, E) // 4,
+                      dtype=torch.int32, device=dev)
+
+    def route_then_index():
+        binding.moe_router_group_limited(idx, wts, scores, bias, wk.n_groups, wk.topk_group,
+                                         wk.norm_weights, wk.scale)
+        binding.moe_create_indices(o1, st1, r1, e1, u1, idx, ws1)
+
+    res["route_then_index_ms"] = run(route_then_index)
+    res["route_and_index_ms"] = run(lambda: binding.moe_route_and_index(
+        idx, wts, o1, st1, r1, e1, u1, scores, bias, tk1, wk.n_groups, wk.topk_group,
+        wk.norm_weights, wk.scale))
+
     dk = wl.WORKLOADS["decode"]
     T, E, K = dk.T, dk.E, dk.K
     s = wl.make_scores(dk).to(dev)
@@ -321,7 +363,7 @@ def extras(wk, scores_h, bias_h, idx, wts, steps):
         binding.moe_finalize(out2, down, r2, w2)
 
     us = graph_replay_us(decode_step)
-    tk = torch.zeros(max(binding.moe_route_and_index_workspace_size(), 4) // 4,
+    tk = torch.zeros(binding.moe_route_and_index_workspace_size(T, K, E) // 4,
                      dtype=torch.int32, device=dev)
 
     def decode_step_fused():

@@ -210,19 +210,27 @@ moe_status_t moe_create_indices_aligned(uint32_t* token_expert_order,
 
 /*
  * moe_route_and_index_workspace_size
- * Bytes of device workspace moe_route_and_index needs: one uint32 counter.
- * Pure host computation; never fails.
+ * Bytes of device workspace moe_route_and_index needs for T tokens, K slots
+ * per token and E experts: a counter word (256 bytes with padding) plus,
+ * when the index step splits the T * K slots into several chunks, its
+ * [chunks, E] uint32 counts matrix. 0 for arguments out of range. Pure host
+ * computation.
  */
-size_t moe_route_and_index_workspace_size(void);
+size_t moe_route_and_index_workspace_size(int64_t T, int32_t K, int32_t E);
 
 /*
  * moe_route_and_index
  * The router (moe_router_group_limited, or moe_router_group_limited_logits
  * when score_fn is not MOE_SCORE_NONE) and moe_create_indices_aligned /
- * moe_create_indices on its expert_indices, in one kernel launch, for
- * small batches where the gap between two launches is a large part of the
- * routing time. Every output is bit-identical to what the two separate
- * calls produce on the same inputs.
+ * moe_create_indices on its expert_indices, with fewer launches. Every
+ * output is bit-identical to what the two separate calls produce on the
+ * same inputs.
+ *   - E a power of two and T * K <= 16384: one launch (the last workgroup
+ *     to finish routing builds the index outputs);
+ *   - otherwise two launches: the router also counts each chunk's slots per
+ *     expert (relaxed atomic adds into the workspace's counts matrix), so
+ *     the index step needs no histogram pass of its own; its last
+ *     workgroup clears the matrix again.
  *
  *   expert_indices, expert_weights       out as moe_router_group_limited.
  *   token_expert_order ... expert_usage_stats
@@ -237,15 +245,14 @@ size_t moe_route_and_index_workspace_size(void);
  *                    MOE_SCORE_SOFTMAX).
  *   expert_bias, scalars                 as moe_router_group_limited.
  *   workspace        device buffer of at least
- *                    moe_route_and_index_workspace_size() bytes, 4-byte
- *                    aligned, ZERO-FILLED before its first use; every call
- *                    leaves it zero again. Calls that share a workspace
- *                    must not run concurrently (one stream, or ordered
- *                    streams).
+ *                    moe_route_and_index_workspace_size(T, K, E) bytes,
+ *                    4-byte aligned, ZERO-FILLED before its first use; every
+ *                    call leaves it zero again (a buffer sized for the
+ *                    largest batch serves every smaller one). Calls that
+ *                    share a workspace must not run concurrently (one
+ *                    stream, or ordered streams).
  *
- * Validation: that of the two separate calls, plus T * K <= 16384 and E
- * a power of two (otherwise MOE_ERR_UNSUPPORTED: the index step runs on
- * one workgroup, and the separate calls serve the rest). With T = 0 only the index
+ * Validation: that of the two separate calls, and the workspace size. With T = 0 only the index
  * metadata outputs are written, as moe_create_indices does for N = 0.
  */
 moe_status_t moe_route_and_index(int32_t* expert_indices, void* expert_weights,

@@ -88,7 +88,7 @@ def load_library(check_runtime: bool = True):
     lib.moe_create_indices_aligned.argtypes = [p, p, p, p, p, p, i64, i32, p, ctypes.c_size_t, p,
                                                ctypes.c_uint32, p]
     lib.moe_create_indices_aligned.restype = ctypes.c_int
-    lib.moe_route_and_index_workspace_size.argtypes = []
+    lib.moe_route_and_index_workspace_size.argtypes = [i64, i32, i32]
     lib.moe_route_and_index_workspace_size.restype = ctypes.c_size_t
     lib.moe_route_and_index.argtypes = [p, p, p, p, p, p, p, p, ctypes.c_uint32, p, p, i32, i32,
                                         i32, i64, i32, i32, i32, i32, i32, ctypes.c_float, i32,
@@ -268,9 +268,11 @@ def moe_create_indices_aligned(token_expert_order: torch.Tensor,
     _check("moe_create_indices_aligned", st)
 
 
-def moe_route_and_index_workspace_size() -> int:
-    """Device workspace bytes moe_route_and_index needs (one counter)."""
-    return int(load_library().moe_route_and_index_workspace_size())
+def moe_route_and_index_workspace_size(T: int, K: int, n_experts: int) -> int:
+    """Device workspace bytes moe_route_and_index needs for T tokens, K slots
+    per token and n_experts experts (a counter and, for batches the index
+    step splits into chunks, its counts matrix)."""
+    return int(load_library().moe_route_and_index_workspace_size(T, K, n_experts))
 
 
 def moe_route_and_index(expert_indices: torch.Tensor, expert_weights: torch.Tensor,
@@ -282,11 +284,11 @@ def moe_route_and_index(expert_indices: torch.Tensor, expert_weights: torch.Tens
                         group_score: int = GROUP_TOP2_SUM, score_fn: int = SCORE_NONE,
                         scales_offset: torch.Tensor = None, scale_align: int = 0,
                         stream=None) -> None:
-    """Router and index creation in one launch (T * K <= 16384). router_input
-    [T, E] holds scores (score_fn SCORE_NONE) or logits; the outputs are those
-    of moe_router_group_limited(_logits) and moe_create_indices(_aligned).
-    workspace: at least moe_route_and_index_workspace_size() bytes, zero
-    before the first call (each call leaves it zero)."""
+    """Router and index creation in one or two launches. router_input [T, E]
+    holds scores (score_fn SCORE_NONE) or logits; the outputs are those of
+    moe_router_group_limited(_logits) and moe_create_indices(_aligned).
+    workspace: at least moe_route_and_index_workspace_size(T, K, E) bytes,
+    zero before the first call (each call leaves it zero)."""
     lib = load_library()
     _dev(expert_indices, expert_weights, token_expert_order, expert_start_indices,
          restore_token_order, expert_ids, expert_usage_stats, router_input, expert_bias,

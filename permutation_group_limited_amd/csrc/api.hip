@@ -75,7 +75,7 @@ static moe_status_t router_common(int32_t* expert_indices, void* expert_weights,
   return launch_router(expert_indices, expert_weights, expert_scores, expert_bias, scores_dtype,
                        bias_dtype, score_fn, T, E, K, n_groups, topk_group, norm_weights ? 1 : 0,
                        routed_scaling_factor, static_cast<int32_t>(group_score),
-                       static_cast<hipStream_t>(stream));
+                       RouterHist{nullptr, 0u}, static_cast<hipStream_t>(stream));
 }
 
 moe_status_t moe_router_group_limited(int32_t* expert_indices, void* expert_weights,
@@ -147,7 +147,7 @@ static moe_status_t indices_common(uint32_t* token_expert_order,
   if (!aligned(workspace, 4)) return MOE_ERR_ALIGNMENT;
   return launch_indices(token_expert_order, expert_start_indices, restore_token_order, expert_ids,
                         expert_usage_stats, scales_offset, scale_align, topk_ids, N, E,
-                        workspace, plan, static_cast<hipStream_t>(stream));
+                        workspace, plan, false, nullptr, static_cast<hipStream_t>(stream));
 }
 
 moe_status_t moe_create_indices(uint32_t* token_expert_order, uint32_t* expert_start_indices,
@@ -174,7 +174,20 @@ moe_status_t moe_create_indices_aligned(uint32_t* token_expert_order,
                         workspace_bytes, scales_offset, scale_align, stream);
 }
 
-size_t moe_route_and_index_workspace_size(void) { return sizeof(uint32_t); }
+// Workspace of moe_route_and_index: a counter word (padded to 256 bytes),
+// then, when the index step has several chunks, its counts matrix. Both are
+// zero between calls.
+static constexpr size_t kTicketBytes = 256;
+
+static size_t route_index_workspace(int64_t N, int32_t E) {
+  const IndexPlan plan = plan_indices(N, E);
+  return kTicketBytes + (plan.nchunks > 1 ? plan.workspace_bytes : 0);
+}
+
+size_t moe_route_and_index_workspace_size(int64_t T, int32_t K, int32_t E) {
+  if (T < 0 || K < 1 || E < 1 || E > 1024 || T > (int64_t)UINT32_MAX / K) return 0;
+  return route_index_workspace(T * K, E);
+}
 
 moe_status_t moe_route_and_index(int32_t* expert_indices, void* expert_weights,
                                  uint32_t* token_expert_order, uint32_t* expert_start_indices,
@@ -199,21 +212,36 @@ moe_status_t moe_route_and_index(int32_t* expert_indices, void* expert_weights,
                            expert_ids, expert_usage_stats, expert_indices, N, E, scales_offset,
                            scale_align);
   if (st != MOE_OK) return st;
-  if (workspace == nullptr || workspace_bytes < sizeof(uint32_t)) return MOE_ERR_WORKSPACE;
+  if (workspace == nullptr || workspace_bytes < route_index_workspace(N, E))
+    return MOE_ERR_WORKSPACE;
   if (!aligned(workspace, 4)) return MOE_ERR_ALIGNMENT;
-  if (N > kRouteIndexMaxSlots || !is_pow2(E)) return MOE_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t* ticket = static_cast<uint32_t*>(workspace);
+  uint32_t* counts = ticket + kTicketBytes / sizeof(uint32_t);
+  const IndexPlan plan = plan_indices(N, E);
   if (T == 0)  // nothing to route: the index step alone writes the metadata
     return launch_indices(token_expert_order, expert_start_indices, restore_token_order,
                           expert_ids, expert_usage_stats, scales_offset, scale_align,
-                          expert_indices, 0, E, nullptr, plan_indices(0, E), s);
-  return launch_route_index(expert_indices, expert_weights, router_input, expert_bias,
-                            input_dtype, bias_dtype, static_cast<int32_t>(score_fn), T, E, K,
-                            n_groups, topk_group, norm_weights ? 1 : 0, routed_scaling_factor,
-                            static_cast<int32_t>(group_score), token_expert_order,
-                            expert_start_indices, restore_token_order, expert_ids,
-                            expert_usage_stats, scales_offset, scale_align,
-                            static_cast<uint32_t*>(workspace), s);
+                          expert_indices, 0, E, nullptr, plan, false, nullptr, s);
+  if (is_pow2(E) && N <= kRouteIndexMaxSlots)  // one launch
+    return launch_route_index(expert_indices, expert_weights, router_input, expert_bias,
+                              input_dtype, bias_dtype, static_cast<int32_t>(score_fn), T, E, K,
+                              n_groups, topk_group, norm_weights ? 1 : 0, routed_scaling_factor,
+                              static_cast<int32_t>(group_score), token_expert_order,
+                              expert_start_indices, restore_token_order, expert_ids,
+                              expert_usage_stats, scales_offset, scale_align, ticket, s);
+  // two launches: the router also fills the index step's counts matrix,
+  // then the scatter (which clears the matrix again) takes no histogram pass
+  const bool multi = plan.nchunks > 1;
+  const moe_status_t rs = launch_router(
+      expert_indices, expert_weights, router_input, expert_bias, input_dtype, bias_dtype,
+      static_cast<int32_t>(score_fn), T, E, K, n_groups, topk_group, norm_weights ? 1 : 0,
+      routed_scaling_factor, static_cast<int32_t>(group_score),
+      RouterHist{multi ? counts : nullptr, static_cast<uint32_t>(plan.chunk)}, s);
+  if (rs != MOE_OK) return rs;
+  return launch_indices(token_expert_order, expert_start_indices, restore_token_order, expert_ids,
+                        expert_usage_stats, scales_offset, scale_align, expert_indices, N, E,
+                        counts, plan, multi, ticket, s);
 }
 
 moe_status_t moe_finalize(void* output, moe_dtype_t out_dtype, const void* down,

@@ -121,12 +121,20 @@ __device__ __forceinline__ uint64_t match_any(uint32_t key, int nbits, uint64_t 
 
 // ---- launchers (host side), one per stage --------------------------------
 
+// Per-chunk expert histogram that the router can fill for the index step:
+// counts is index creation's counts matrix [nchunks, E] (uint32, zero on
+// entry), chunk its slots per chunk. counts == NULL: no histogram.
+struct RouterHist {
+  uint32_t* counts;
+  uint32_t chunk;
+};
+
 // score_fn: 0 = scores given, 1 = sigmoid of logits, 2 = softmax of logits
 moe_status_t launch_router(int32_t* expert_indices, void* expert_weights, const void* scores,
                            const void* bias, moe_dtype_t scores_dtype, moe_dtype_t bias_dtype,
                            int32_t score_fn, int64_t T, int32_t E, int32_t K, int32_t n_groups,
                            int32_t topk_group, int32_t norm_weights, float scale, int32_t mode,
-                           hipStream_t stream);
+                           RouterHist hist, hipStream_t stream);
 
 struct IndexPlan {
   int waves;        // waves per workgroup (16 when E <= 256, else 4)
@@ -137,12 +145,17 @@ struct IndexPlan {
 };
 IndexPlan plan_indices(int64_t N, int32_t E);
 
-// scales_offset may be NULL (then scale_align is ignored)
+// scales_offset may be NULL (then scale_align is ignored). With
+// counts_ready the counts matrix in `workspace` was already filled (by the
+// router) and the histogram launch is skipped; the scatter then counts its
+// workgroups on `ticket` and the last one clears the matrix and the ticket
+// for the next call.
 moe_status_t launch_indices(uint32_t* token_expert_order, uint32_t* expert_start_indices,
                             uint32_t* restore_token_order, int32_t* expert_ids,
                             uint32_t* expert_usage_stats, uint32_t* scales_offset,
                             uint32_t scale_align, const int32_t* topk_ids, int64_t N, int32_t E,
-                            void* workspace, const IndexPlan& plan, hipStream_t stream);
+                            void* workspace, const IndexPlan& plan, bool counts_ready,
+                            uint32_t* ticket, hipStream_t stream);
 
 // Router and index creation in one launch: every workgroup routes its
 // tokens, then the last one to finish (counted on `ticket`, one uint32 that

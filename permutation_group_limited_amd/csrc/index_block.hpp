@@ -96,13 +96,21 @@ __device__ __forceinline__ void load_batch(int32_t (&ev)[kBatch], const int32_t*
 // scatter; chunk 0 also writes expert_ids, expert_start_indices, the stats
 // and, when asked, the aligned scale offsets. Must be reached by every
 // thread of the workgroup.
+//
+// ticket != NULL (several chunks, counts filled by the router's atomics):
+// after its scatter, thread 0 adds one to *ticket; the workgroup that draws
+// the last ticket clears the matrix (nchunks * E words) and the ticket, so
+// that both are zero for the next call. Only a read-before-write order is
+// needed (every workgroup has consumed its loads of the matrix before its
+// add, and the clearing stores are issued after the last add returns), so
+// the add is relaxed: no cache write-back or invalidation per workgroup.
 template <int W>
 __device__ __forceinline__ void scatter_chunk(
     uint32_t* __restrict__ order, uint32_t* __restrict__ starts, uint32_t* __restrict__ restore,
     int32_t* __restrict__ expert_ids, uint32_t* __restrict__ stats,
     uint32_t* __restrict__ scales_offset, uint32_t scale_align,
     const int32_t* __restrict__ ids, const uint32_t* __restrict__ counts, int64_t N, int32_t E,
-    int64_t chunk, int64_t nchunks, int rounds, int64_t chunk_id) {
+    int64_t chunk, int64_t nchunks, int rounds, int64_t chunk_id, uint32_t* ticket = nullptr) {
   constexpr int kThreads = W * kWave;
   constexpr int kMaxEPT = (kMaxExperts + kThreads - 1) / kThreads;
   static_assert(kMaxEPT * W <= 16, "an owned expert's per-wave counts live in registers");
@@ -348,6 +356,19 @@ __device__ __forceinline__ void scatter_chunk(
       }
     }
   }
+  if (ticket == nullptr) return;  // uniform
+  __shared__ uint32_t is_last;
+  if (threadIdx.x == 0)
+    is_last = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                      static_cast<uint32_t>(nchunks - 1)
+                  ? 1u
+                  : 0u;
+  __syncthreads();
+  if (is_last == 0u) return;  // uniform
+  uint32_t* clear = const_cast<uint32_t*>(counts);
+  for (int64_t x = threadIdx.x; x < nchunks * E; x += kThreads) clear[x] = 0u;
+  if (threadIdx.x == 0)
+    __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace

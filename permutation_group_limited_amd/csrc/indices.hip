@@ -73,10 +73,10 @@ __global__ __launch_bounds__(W * kWave) void index_scatter_kernel(
     uint32_t* __restrict__ order, uint32_t* __restrict__ starts, uint32_t* __restrict__ restore,
     int32_t* __restrict__ expert_ids, uint32_t* __restrict__ stats,
     uint32_t* __restrict__ scales_offset, uint32_t scale_align,
-    const int32_t* __restrict__ ids, const uint32_t* __restrict__ counts, int64_t N, int32_t E,
-    int64_t chunk, int64_t nchunks, int rounds) {
+    const int32_t* __restrict__ ids, uint32_t* counts, int64_t N, int32_t E, int64_t chunk,
+    int64_t nchunks, int rounds, uint32_t* ticket) {
   scatter_chunk<W>(order, starts, restore, expert_ids, stats, scales_offset, scale_align, ids,
-                   counts, N, E, chunk, nchunks, rounds, blockIdx.x);
+                   counts, N, E, chunk, nchunks, rounds, blockIdx.x, ticket);
 }
 
 }  // namespace
@@ -109,8 +109,9 @@ template <int W>
 moe_status_t launch_indices_t(uint32_t* order, uint32_t* starts, uint32_t* restore,
                               int32_t* expert_ids, uint32_t* stats, uint32_t* scales,
                               uint32_t align, const int32_t* ids, int64_t N, int32_t E,
-                              uint32_t* counts, const IndexPlan& plan, hipStream_t stream) {
-  if (plan.nchunks > 1) {
+                              uint32_t* counts, const IndexPlan& plan, bool counts_ready,
+                              uint32_t* ticket, hipStream_t stream) {
+  if (plan.nchunks > 1 && !counts_ready) {
     hipLaunchKernelGGL(index_hist_kernel<W>, dim3(static_cast<uint32_t>(plan.nchunks)),
                        dim3(W * kWave), 0, stream, counts, ids, N, E, plan.chunk, plan.rounds);
     const moe_status_t st = check_launch();
@@ -118,8 +119,8 @@ moe_status_t launch_indices_t(uint32_t* order, uint32_t* starts, uint32_t* resto
   }
   hipLaunchKernelGGL(index_scatter_kernel<W>, dim3(static_cast<uint32_t>(plan.nchunks)),
                      dim3(W * kWave), 0, stream, order, starts, restore, expert_ids, stats, scales,
-                     align, ids, static_cast<const uint32_t*>(counts), N, E, plan.chunk,
-                     plan.nchunks, plan.rounds);
+                     align, ids, counts, N, E, plan.chunk, plan.nchunks, plan.rounds,
+                     counts_ready && plan.nchunks > 1 ? ticket : nullptr);
   return check_launch();
 }
 }  // namespace
@@ -127,13 +128,14 @@ moe_status_t launch_indices_t(uint32_t* order, uint32_t* starts, uint32_t* resto
 moe_status_t launch_indices(uint32_t* order, uint32_t* starts, uint32_t* restore,
                             int32_t* expert_ids, uint32_t* stats, uint32_t* scales,
                             uint32_t align, const int32_t* ids, int64_t N, int32_t E,
-                            void* workspace, const IndexPlan& plan, hipStream_t stream) {
+                            void* workspace, const IndexPlan& plan, bool counts_ready,
+                            uint32_t* ticket, hipStream_t stream) {
   uint32_t* counts = static_cast<uint32_t*>(workspace);
   if (plan.waves == 16)
     return launch_indices_t<16>(order, starts, restore, expert_ids, stats, scales, align, ids, N,
-                                E, counts, plan, stream);
+                                E, counts, plan, counts_ready, ticket, stream);
   return launch_indices_t<4>(order, starts, restore, expert_ids, stats, scales, align, ids, N, E,
-                             counts, plan, stream);
+                             counts, plan, counts_ready, ticket, stream);
 }
 
 }  // namespace moe

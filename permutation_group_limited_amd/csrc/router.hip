@@ -35,23 +35,24 @@ __global__ __launch_bounds__(kBlock) void router_kernel(
     int32_t* __restrict__ out_idx, typename DS::storage* __restrict__ out_w,
     const typename DS::storage* __restrict__ scores, const typename DB::storage* __restrict__ bias,
     int64_t T, int32_t K, int32_t n_groups, int32_t topk_group, int32_t norm_weights,
-    float scale, int32_t mode) {
+    float scale, int32_t mode, RouterHist hist) {
   route_tokens<DS, DB, EPL, LPT, FN, kWavesPerBlock>(out_idx, out_w, scores, bias, T, K, n_groups,
-                                                     topk_group, norm_weights, scale, mode);
+                                                     topk_group, norm_weights, scale, mode, 0,
+                                                     hist);
 }
 
 template <typename DS, typename DB, int EPL, int LPT, int FN>
 struct RouterLaunch {
   static moe_status_t run(int32_t* idx, void* w, const void* s, const void* b, int64_t T,
                           int32_t K, int32_t G, int32_t TG, int32_t norm, float scale,
-                          int32_t mode, hipStream_t stream) {
+                          int32_t mode, RouterHist hist, hipStream_t stream) {
     constexpr int TPB = kWavesPerBlock * (kWave / LPT);  // tokens per block
     const int64_t blocks = (T + TPB - 1) / TPB;
     hipLaunchKernelGGL((router_kernel<DS, DB, EPL, LPT, FN>), dim3(static_cast<uint32_t>(blocks)),
                        dim3(kBlock), 0, stream, idx, static_cast<typename DS::storage*>(w),
                        static_cast<const typename DS::storage*>(s),
                        static_cast<const typename DB::storage*>(b), T, K, G, TG, norm, scale,
-                       mode);
+                       mode, hist);
     return check_launch();
   }
 };
@@ -63,9 +64,10 @@ __global__ __launch_bounds__(kBlock) void router_any_e_kernel(
     int32_t* __restrict__ out_idx, typename DS::storage* __restrict__ out_w,
     const typename DS::storage* __restrict__ scores, const typename DB::storage* __restrict__ bias,
     int64_t T, int32_t K, int32_t n_groups, int32_t topk_group, int32_t norm_weights,
-    float scale, int32_t mode, int32_t E) {
+    float scale, int32_t mode, int32_t E, RouterHist hist) {
   route_tokens<DS, DB, EPL, kWave, FN, kWavesPerBlock, true>(
-      out_idx, out_w, scores, bias, T, K, n_groups, topk_group, norm_weights, scale, mode, E);
+      out_idx, out_w, scores, bias, T, K, n_groups, topk_group, norm_weights, scale, mode, E,
+      hist);
 }
 
 // Reached through dispatch_router with the padded expert count
@@ -74,7 +76,7 @@ template <typename DS, typename DB, int EPL, int LPT, int FN>
 struct RouterAnyELaunch {
   static moe_status_t run(int32_t* idx, void* w, const void* s, const void* b, int64_t T,
                           int32_t K, int32_t G, int32_t TG, int32_t norm, float scale,
-                          int32_t mode, int32_t E, hipStream_t stream) {
+                          int32_t mode, int32_t E, RouterHist hist, hipStream_t stream) {
     if constexpr (LPT != kWave) {
       return MOE_ERR_UNSUPPORTED;
     } else {
@@ -84,7 +86,7 @@ struct RouterAnyELaunch {
                          static_cast<typename DS::storage*>(w),
                          static_cast<const typename DS::storage*>(s),
                          static_cast<const typename DB::storage*>(b), T, K, G, TG, norm, scale,
-                         mode, E);
+                         mode, E, hist);
       return check_launch();
     }
   }
@@ -95,14 +97,14 @@ struct RouterAnyELaunch {
 moe_status_t launch_router(int32_t* idx, void* w, const void* s, const void* b,
                            moe_dtype_t sd, moe_dtype_t bd, int32_t fn, int64_t T, int32_t E,
                            int32_t K, int32_t G, int32_t TG, int32_t norm, float scale,
-                           int32_t mode, hipStream_t stream) {
+                           int32_t mode, RouterHist hist, hipStream_t stream) {
   if ((E & (E - 1)) == 0)
     return dispatch_router<RouterLaunch>(sd, bd, fn, E, idx, w, s, b, T, K, G, TG, norm, scale,
-                                         mode, stream);
+                                         mode, hist, stream);
   int32_t padded = kWave;
   while (padded < E) padded <<= 1;
   return dispatch_router<RouterAnyELaunch>(sd, bd, fn, padded, idx, w, s, b, T, K, G, TG, norm,
-                                           scale, mode, E, stream);
+                                           scale, mode, E, hist, stream);
 }
 
 }  // namespace moe

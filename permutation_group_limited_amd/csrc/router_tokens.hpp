@@ -187,7 +187,7 @@ __device__ __forceinline__ void route_tokens(
     int32_t* __restrict__ out_idx, typename DS::storage* __restrict__ out_w,
     const typename DS::storage* __restrict__ scores, const typename DB::storage* __restrict__ bias,
     int64_t T, int32_t K, int32_t n_groups, int32_t topk_group, int32_t norm_weights,
-    float scale, int32_t mode, int32_t E_rt = 0) {
+    float scale, int32_t mode, int32_t E_rt = 0, RouterHist hist = RouterHist{nullptr, 0u}) {
   static_assert(!GEN || LPT == kWave, "the general-E form routes one token per wave");
   const int32_t E = GEN ? E_rt : EPL * LPT;
   constexpr int TPW = kWave / LPT;  // tokens per wave
@@ -384,6 +384,13 @@ __device__ __forceinline__ void route_tokens(
   if (slot) {
     out_idx[t * K + sub] = static_cast<int32_t>(my_id);
     out_w[t * K + sub] = to_storage<DS>(w);
+  }
+  // histogram of the index step: one counter per (chunk, expert), summed
+  // with relaxed atomics (integer sums do not depend on their order)
+  if (hist.counts != nullptr && slot) {  // the pointer test is uniform
+    const uint32_t i = static_cast<uint32_t>(t * K + sub);
+    __hip_atomic_fetch_add(hist.counts + static_cast<size_t>(i / hist.chunk) * E + my_id, 1u,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

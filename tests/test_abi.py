@@ -1,6 +1,8 @@
 """The C-ABI library: it loads, exports every entry point that
 include/moe_route.h declares, and rejects bad arguments on the host before
-any launch (these calls never reach the GPU, so they run on the CPU)."""
+any launch. Every call here either fails validation or returns before a
+launch (T = 0 router / finalize calls), so no kernel ever sees the fake
+pointers; these tests run on the CPU."""
 import ctypes
 import os
 import re
@@ -156,7 +158,7 @@ def test_aligned_indices_validation(lib):
 
 
 def route_index(lib, T=16, E=256, K=8, G=8, TG=4, fn=0, sd=0, bd=0, mode=0, ws=FAKE,
-                ws_bytes=4, scales=None, align=0, ptrs=None):
+                ws_bytes=1 << 20, scales=None, align=0, ptrs=None):
     p = ptrs or (FAKE,) * 9
     return lib.moe_route_and_index(p[0], p[1], p[2], p[3], p[4], p[5], p[6], scales, align,
                                    p[7], p[8], sd, bd, fn, T, E, K, G, TG, 1,
@@ -164,14 +166,20 @@ def route_index(lib, T=16, E=256, K=8, G=8, TG=4, fn=0, sd=0, bd=0, mode=0, ws=F
 
 
 def test_route_and_index_workspace_size(lib):
-    assert lib.moe_route_and_index_workspace_size() == 4
+    ws = lib.moe_route_and_index_workspace_size
+    # a counter (256 bytes padded) and, for several index chunks, the counts
+    assert ws(128, 8, 256) == 256
+    assert ws(8192, 8, 256) == 256 + lib.moe_create_indices_workspace_size(65536, 256)
+    assert ws(8192, 8, 256) > 256
+    assert ws(100, 6, 160) == 256
+    assert ws(-1, 8, 256) == 0 and ws(8, 0, 256) == 0 and ws(8, 8, 2048) == 0
 
 
 @pytest.mark.parametrize("kw,code", [
     # router checks
     (dict(T=-1), INVALID), (dict(G=3), INVALID), (dict(K=0), INVALID), (dict(TG=9), INVALID),
     (dict(mode=2), INVALID), (dict(fn=3), INVALID), (dict(sd=1, bd=2), UNSUPPORTED),
-    (dict(E=96, G=8), UNSUPPORTED), (dict(E=2048, G=8), UNSUPPORTED),
+    (dict(E=2048, G=8), UNSUPPORTED),
     (dict(ptrs=(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE_MIS, FAKE)), ALIGNMENT),
     (dict(ptrs=(None,) + (FAKE,) * 8), INVALID),
     # index-output checks
@@ -180,9 +188,8 @@ def test_route_and_index_workspace_size(lib):
     (dict(ptrs=(FAKE,) * 6 + (FAKE_ODD, FAKE, FAKE)), ALIGNMENT),
     (dict(scales=FAKE, align=0), INVALID), (dict(scales=FAKE_ODD, align=4), ALIGNMENT),
     # workspace
-    (dict(ws=None), WORKSPACE), (dict(ws_bytes=3), WORKSPACE), (dict(ws=FAKE_ODD), ALIGNMENT),
-    # batch size: the index step runs on one workgroup
-    (dict(T=2049, K=8), UNSUPPORTED), (dict(T=16385, E=8, G=1, TG=1, K=1), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=255), WORKSPACE), (dict(ws=FAKE_ODD), ALIGNMENT),
+    (dict(T=8192, ws_bytes=256), WORKSPACE),  # several index chunks need the counts matrix
 ])
 def test_route_and_index_validation(lib, kw, code):
     assert route_index(lib, **kw) == code

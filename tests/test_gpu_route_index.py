@@ -1,6 +1,8 @@
-"""GPU parity of moe_route_and_index (router and index creation in one
-launch) against the oracle's router followed by its index creation, and
-bit-identity with the two separate GPU entry points on the same inputs.
+"""GPU parity of moe_route_and_index (router and index creation with fewer
+launches: one for small power-of-two-E batches, else the router filling the
+index step's histogram, then the scatter) against the oracle's router
+followed by its index creation, and bit-identity with the two separate GPU
+entry points on the same inputs; the workspace is all zero after each call.
 
 Acceptance as for the separate stages: indices and every index output
 bit-exact; fp32 weights within 1e-6 relative, 16-bit weights within 1 ulp
@@ -57,14 +59,25 @@ def launch(o, x, b, ws, G, TG, norm, scale, fn, mode=0, align=0, stream=None):
                                 scales_offset=o.scales, scale_align=align, stream=stream)
 
 
+def workspace(T, K, E):
+    n = binding.moe_route_and_index_workspace_size(T, K, E)
+    assert n >= 256 and n % 4 == 0
+    return torch.zeros(n // 4, dtype=torch.int32, device=DEV)
+
+
+def assert_zero(ws, what=""):
+    nz = int(torch.count_nonzero(ws).item())
+    assert nz == 0, "workspace not left zero (%d words set) %s" % (nz, what)
+
+
 def fused(x, b, K, G, TG, norm, scale, fn="none", mode=0, align=0, ws=None):
     """One fused call on host inputs; checks the workspace is left zero."""
     T, E = x.shape
     o = Outputs(T, E, K, x.dtype, align > 0)
-    ws = torch.zeros(1, dtype=torch.int32, device=DEV) if ws is None else ws
+    ws = workspace(T, K, E) if ws is None else ws
     launch(o, x.to(DEV), b.to(DEV), ws, G, TG, norm, scale, FNS[fn][0], mode, align)
     torch.cuda.synchronize()
-    assert int(ws.item()) == 0, "workspace counter not left at zero"
+    assert_zero(ws)
     return o.host()
 
 
@@ -118,7 +131,9 @@ def check_same(a, b_):
 
 
 @pytest.mark.parametrize("name,T", [("decode", 128), ("tiny", 64), ("mixtral", 2048),
-                                    ("dsv3", 2048), ("dsv3", 1), ("decode", 97)])
+                                    ("dsv3", 2048), ("dsv3", 1), ("decode", 97),
+                                    ("mixtral", 4096), ("dsv3", 8192), ("dsv3", 3001),
+                                    ("skewed", 65536)])
 @pytest.mark.parametrize("from_logits", [False, True])
 def test_workload_shapes(name, T, from_logits):
     wk = wl.WORKLOADS[name].with_tokens(T)
@@ -137,7 +152,11 @@ def test_workload_shapes(name, T, from_logits):
 @pytest.mark.parametrize("T,E,G,TG,K", [(1, 1, 1, 1, 1), (33, 2, 1, 1, 2), (129, 8, 4, 2, 3),
                                         (300, 32, 8, 4, 6), (77, 64, 8, 3, 6),
                                         (511, 128, 8, 4, 8), (1000, 256, 8, 4, 8),
-                                        (61, 512, 16, 4, 8), (2048, 1024, 16, 4, 8)])
+                                        (61, 512, 16, 4, 8), (2048, 1024, 16, 4, 8),
+                                        # two launches: several chunks, or E not a power of two
+                                        (5000, 1024, 16, 4, 8), (2500, 8, 1, 1, 8),
+                                        (100, 160, 8, 3, 6), (4096, 160, 8, 3, 6),
+                                        (777, 20, 4, 3, 6), (3000, 1000, 8, 4, 8)])
 @pytest.mark.parametrize("levels", [0, 3])
 def test_random_shapes(T, E, G, TG, K, levels):
     log("route_and_index random", T, E, G, TG, K, levels)
@@ -191,11 +210,12 @@ def test_empty_batch():
 
 def test_back_to_back_calls_share_the_counter():
     """Calls queued without synchronisation on one workspace, with sizes
-    going down and up: each must see the counter the previous one left."""
+    going down and up and switching between the one- and two-launch forms:
+    each must see the counter and counts the previous one left."""
     wk = wl.WORKLOADS["decode"]
     log("route_and_index back to back")
-    ws = torch.zeros(1, dtype=torch.int32, device=DEV)
-    Ts = [128, 3, 2000, 17, 128, 1]
+    ws = workspace(8192, wk.K, wk.E)
+    Ts = [128, 3, 2000, 8192, 17, 5000, 128, 1, 8192]
     cases = []
     for i, T in enumerate(Ts):
         x = wl.random_scores(T, wk.E, seed=100 + i, levels=4 if i % 2 else 0)
@@ -204,19 +224,20 @@ def test_back_to_back_calls_share_the_counter():
         launch(o, x.to(DEV), b.to(DEV), ws, 8, 4, True, 2.5, binding.SCORE_NONE)
         cases.append((x, b, o))
     torch.cuda.synchronize()
-    assert int(ws.item()) == 0
+    assert_zero(ws)
     for x, b, o in cases:
         check_against_oracle(o.host(), x, b, wk.K, 8, 4, True, 2.5)
 
 
-def test_graph_replay():
+@pytest.mark.parametrize("name", ["decode", "dsv3"])
+def test_graph_replay(name):
     """Captured once, replayed several times with eager work in between;
-    every replay gives the eager result and leaves the counter at zero."""
-    wk = wl.WORKLOADS["decode"]
-    log("route_and_index graph replay")
+    every replay gives the eager result and leaves the workspace zero."""
+    wk = wl.WORKLOADS[name]
+    log("route_and_index graph replay", name)
     x = wl.make_scores(wk).to(DEV)
     b = wl.make_bias(wk).to(DEV)
-    ws = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ws = workspace(wk.T, wk.K, wk.E)
     eager = Outputs(wk.T, wk.E, wk.K, torch.float32, True)
     launch(eager, x, b, ws, 8, 4, True, 2.5, binding.SCORE_NONE, align=16)
     torch.cuda.synchronize()
@@ -239,5 +260,5 @@ def test_graph_replay():
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        assert int(ws.item()) == 0, "replay %d left the counter set" % rep
+        assert_zero(ws, "after replay %d" % rep)
         check_same(o.host(), ref)
