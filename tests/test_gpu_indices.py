@@ -113,3 +113,46 @@ def test_aligned_scale_offsets(N, E, align):
     got, scales = gpu_indices_aligned(ids, E, align)
     assert_indices_equal(got, oracle.create_indices(ids, E))
     assert np.array_equal(scales, oracle.scale_offsets(ids, E, align))
+
+
+@pytest.mark.parametrize("N,E", [((1 << 28) + 12345, 256), ((1 << 27) + 7, 1000)])
+def test_huge_n_properties(N, E):
+    """Far past what the oracle finishes: 2^28 + 12345 slots (outputs are
+    uint32, so N may go up to 2^32 - 1). Checked on the GPU through the
+    properties that define the result: token_expert_order is a permutation
+    and restore_token_order its inverse; read through the order, the ids are
+    non-decreasing and, within one expert, the slot indices ascend (stable);
+    expert_start_indices, expert_ids and expert_usage_stats equal what
+    torch.bincount gives."""
+    log("indices huge N", N, "E", E)
+    dev = "cuda:0"
+    g = torch.Generator(device=dev).manual_seed(N % 1000003)
+    ids = torch.randint(0, E, (N,), generator=g, dtype=torch.int32, device=dev)
+    order = torch.full((N,), -1, dtype=torch.int32, device=dev)
+    restore = torch.full((N,), -1, dtype=torch.int32, device=dev)
+    starts = torch.full((E + 1,), -1, dtype=torch.int32, device=dev)
+    eids = torch.full((E,), -7, dtype=torch.int32, device=dev)
+    stats = torch.full((2,), -1, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(binding.moe_create_indices_workspace_size(N, E), 4) // 4,
+                     dtype=torch.int32, device=dev)
+    binding.moe_create_indices(order, starts, restore, eids, stats, ids, ws)
+    torch.cuda.synchronize()
+    o = order.long()
+    assert int(o.min()) == 0 and int(o.max()) == N - 1
+    assert torch.equal(restore.long()[o], torch.arange(N, device=dev))
+    seg = ids[o]
+    assert bool((seg[1:] >= seg[:-1]).all())
+    same = seg[1:] == seg[:-1]
+    assert bool((o[1:] > o[:-1])[same].all())
+    del seg, same
+    cnt = torch.bincount(ids.long(), minlength=E)
+    active = torch.nonzero(cnt).flatten()
+    A = active.numel()
+    csum = torch.cat([torch.zeros(1, dtype=torch.long, device=dev), torch.cumsum(cnt, 0)])
+    exp_starts = torch.full((E + 1,), N, dtype=torch.long, device=dev)
+    exp_starts[:A] = csum[active]
+    assert torch.equal(starts.long(), exp_starts)
+    exp_ids = torch.full((E,), -1, dtype=torch.long, device=dev)
+    exp_ids[:A] = active
+    assert torch.equal(eids.long(), exp_ids)
+    assert stats.tolist() == [int(cnt.max()), A]

@@ -162,3 +162,24 @@ def test_logits_random_shapes(fn, T, E, G, TG, K, dt):
             assert_weights_close(gw, ow)
         else:
             assert_16bit_within_one_ulp(bf16_bits(gw), ow, "router weights")
+
+
+def test_huge_batch_sampled():
+    """2^20 + 3 tokens of the DSv3 shape (1 GiB of scores), routed in one
+    call; each token's result depends on its own row only, so the oracle
+    checks 4,099 of them (random rows, the first and the last)."""
+    T, E, K, G, TG = (1 << 20) + 3, 256, 8, 8, 4
+    log("router huge batch", T)
+    dev = "cuda:0"
+    g = torch.Generator(device=dev).manual_seed(11)
+    s = torch.sigmoid(torch.randn(T, E, generator=g, device=dev))
+    b = wl.random_bias(E, seed=12).to(dev)
+    idx = torch.full((T, K), -7, dtype=torch.int32, device=dev)
+    w = torch.full((T, K), float("nan"), device=dev)
+    binding.moe_router_group_limited(idx, w, s, b, G, TG, True, 2.5)
+    torch.cuda.synchronize()
+    rows = torch.randperm(T, generator=torch.Generator().manual_seed(13))[:4096]
+    rows = torch.cat([rows, torch.tensor([0, 1, T - 1])]).to(dev)
+    oi, ow = oracle.router(s[rows].cpu().numpy(), b.cpu().numpy(), K, G, TG, True, 2.5)
+    assert np.array_equal(idx[rows].cpu().numpy(), oi)
+    assert_weights_close(w[rows].cpu().numpy(), ow)
