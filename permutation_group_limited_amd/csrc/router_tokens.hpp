@@ -385,12 +385,45 @@ __device__ __forceinline__ void route_tokens(
     out_idx[t * K + sub] = static_cast<int32_t>(my_id);
     out_w[t * K + sub] = to_storage<DS>(w);
   }
-  // histogram of the index step: one counter per (chunk, expert), summed
-  // with relaxed atomics (integer sums do not depend on their order)
-  if (hist.counts != nullptr && slot) {  // the pointer test is uniform
-    const uint32_t i = static_cast<uint32_t>(t * K + sub);
-    __hip_atomic_fetch_add(hist.counts + static_cast<size_t>(i / hist.chunk) * E + my_id, 1u,
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // Histogram of the index step: one counter per (chunk, expert), summed
+  // with relaxed atomics (integer sums do not depend on their order). Same-
+  // address device-scope atomics serialise, and a popular expert appears in
+  // most tokens, so the workgroup first merges its slots: each slot's key
+  // (chunk offset from the workgroup's first chunk, expert) goes to LDS in
+  // slot order, then wave 0 groups equal keys (peer masks from ballots) and
+  // one lane per distinct key issues the global add. A workgroup holds at
+  // most 256 slots and a chunk at least 256, so the offset is 0 or 1.
+  if (hist.counts != nullptr) {  // uniform
+    constexpr int kThreads = WPB * kWave;
+    __shared__ uint32_t keys[kThreads];
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * WPB * TPW;  // first token
+    const int64_t t1 = (t0 + WPB * TPW < T) ? t0 + WPB * TPW : T;
+    const int nslots = static_cast<int>((t1 - t0) * K);
+    const uint32_t c0 = static_cast<uint32_t>((t0 * K) / hist.chunk);
+    if (slot) {
+      const uint32_t dc = static_cast<uint32_t>(t * K + sub) / hist.chunk - c0;
+      if (dc < 2u) {
+        keys[(t - t0) * K + sub] = (dc << 10) | my_id;
+      } else {  // not reached with the launch shapes used; kept correct anyway
+        keys[(t - t0) * K + sub] = 0xFFFFFFFFu;
+        __hip_atomic_fetch_add(hist.counts + static_cast<size_t>(c0 + dc) * E + my_id, 1u,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      for (int r = 0; r < nslots; r += kWave) {
+        const uint32_t key =
+            r + lane < nslots ? keys[r + lane] : 0xFFFFFFFFu;
+        const bool ok = key != 0xFFFFFFFFu;
+        const uint64_t peers = match_any(key, 11, __ballot(ok));
+        if (ok && (__ffsll(static_cast<unsigned long long>(peers)) - 1) == lane)
+          __hip_atomic_fetch_add(
+              hist.counts + static_cast<size_t>(c0 + (key >> 10)) * E + (key & 1023u),
+              static_cast<uint32_t>(__popcll(peers)), __ATOMIC_RELAXED,
+              __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
   }
 }
 
