@@ -21,7 +21,10 @@
 //      term from a ballot-built peer mask and mbcnt. Workgroup 0 also writes
 //      expert_ids, expert_start_indices and the stats (and, when asked, the
 //      aligned scale offsets).
-// A problem that fits one chunk skips step 1 (one launch in total).
+// A problem that fits one chunk skips step 1 (one launch in total). When
+// moe_route_and_index runs the path, the router fills the counts matrix
+// itself (relaxed atomic adds) and step 1 is skipped too; the scatter's
+// last workgroup then clears the matrix for the next call.
 //
 // Both kernels are latency-bound (N * 12 bytes in all), so every wave issues
 // all of its id loads (up to 8 rounds of 64) before using any, keeps them in
