@@ -37,6 +37,25 @@ def test_f16_rounding_matches_numpy(oracle):
     assert np.all(np.isnan(got[nan].view(np.float16)))
 
 
+def test_f16_values_and_midpoints(oracle):
+    # every binary16 value is its own rounding (widen, then narrow), and every
+    # midpoint between neighbours, max finite to infinity included, rounds as
+    # numpy does (ties to even)
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    v = bits.view(np.float16)
+    fin = np.isfinite(v)
+    wide = oracle.f16_to_f32(bits[fin])
+    assert np.array_equal(oracle.f32_to_f16(wide), bits[fin])
+    pos = np.sort(v[fin & (v >= 0)].astype(np.float64))
+    nxt = np.append(pos[1:], 65536.0)  # the next value above 65504 is infinity's threshold
+    mids = ((pos + nxt) / 2).astype(np.float32)
+    assert np.all(mids.astype(np.float64) == (pos + nxt) / 2)  # exact in binary32
+    with np.errstate(over="ignore"):
+        ref = mids.astype(np.float16).view(np.uint16)
+    assert np.array_equal(oracle.f32_to_f16(mids), ref)
+    assert np.array_equal(oracle.f32_to_f16(-mids), ref | 0x8000)
+
+
 @pytest.mark.parametrize("sd,bd", [("bf16", "bf16"), ("bf16", "f32"), ("f16", "f16"),
                                    ("f16", "f32")])
 def test_router_16bit_equals_fp32_on_widened_values(oracle, sd, bd):

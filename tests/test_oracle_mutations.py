@@ -16,6 +16,8 @@ SRC = os.path.join(ROOT, "oracle", "moe_oracle.c")
 ROUTER = "tests/test_oracle_router.py"
 INDICES = "tests/test_oracle_indices.py"
 FINALIZE = "tests/test_oracle_finalize.py"
+DTYPES = "tests/test_oracle_dtypes.py"
+SCOREFN = "tests/test_oracle_scorefn.py"
 
 MUTATIONS = [
     ("bias left out of the selection", ROUTER,
@@ -77,6 +79,25 @@ MUTATIONS = [
      "int64_t row = 0;\n                    for (int64_t q = 0; q < N; ++q) if (restore_order[q] == (uint32_t)(t * K + k)) row = q;"),
     ("bf16 conversion truncates", FINALIZE, "u += 0x7fffu + lsb;", "(void)lsb;"),
     ("bf16 ties rounded away from zero", FINALIZE, "u += 0x7fffu + lsb;", "u += 0x8000u; (void)lsb;"),
+    ("binary16 rounding truncates", DTYPES,
+     "const uint32_t rounded = a + 0x0fffu + ((a >> 13) & 1u);", "const uint32_t rounded = a;"),
+    ("binary16 ties rounded away from zero", DTYPES,
+     "a + 0x0fffu + ((a >> 13) & 1u)", "a + 0x1000u"),
+    ("binary16 subnormals truncated", DTYPES, "(uint16_t)nearbyintf(scaled)", "(uint16_t)scaled"),
+    ("binary16 overflow threshold too low", DTYPES, "if (a >= 0x477ff000u)",
+     "if (a >= 0x477fe000u)"),
+    ("binary16 exponent rebias off by one", DTYPES, "((ex + 112u) << 23)", "((ex + 111u) << 23)"),
+    ("binary16 output through bf16 rounding", DTYPES,
+     "((uint16_t*)p)[i] = moe_oracle_f32_to_f16(v);", "((uint16_t*)p)[i] = moe_oracle_f32_to_bf16(v);"),
+    ("bias read in the scores' dtype", DTYPES,
+     "b[e] = s[e] + load_as_f32(bias, bias_dtype, e);",
+     "b[e] = s[e] + load_as_f32(bias, scores_dtype, e);"),
+    ("sigmoid of the negated logit", SCOREFN, "exp(-(double)s[e])", "exp((double)s[e])"),
+    ("softmax sum misses the last expert", SCOREFN,
+     "for (int32_t e = 0; e < E; ++e) sum += exp((double)s[e] - m);",
+     "for (int32_t e = 0; e + 1 < E; ++e) sum += exp((double)s[e] - m);"),
+    ("softmax evaluated in binary32", SCOREFN,
+     "s[e] = (float)(exp((double)s[e] - m) / sum);", "s[e] = expf(s[e] - (float)m) / (float)sum;"),
 ]
 
 
