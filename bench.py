@@ -22,9 +22,13 @@ Reported beside the throughput:
     its mean duration above, against 8 TB/s; plus the HBM bytes measured by
     rocprofv3 counters when the committed counter summary matches the
     current kernel source;
+  * protocol: the step and each stage captured in HIP graphs, replayed with
+    a cold cache (1 GiB written before each replay, outside the events) and
+    warm, median / minimum; a 1 GiB device-copy bandwidth probe;
   * cpu_baseline: the CPU oracle (plain C, OpenMP over tokens) timed on the
-    host cores over whole steps of the same workload, and a parity check of
-    the GPU step against it.
+    host cores over whole steps of the same workload, per stage on all
+    threads and on one thread, and a parity check of the GPU step against
+    it.
 """
 from __future__ import annotations
 
@@ -235,6 +239,9 @@ def main():
     }
 
     if not args.no_extras:
+        result["protocol"] = timing_protocol(
+            step, {"router": router, "create_indices": indices,
+                   "route_and_index": route_and_index, "finalize": finalize})
         result["extras"] = extras(wk, scores_h, bias_h, idx, wts, args.steps)
 
     if args.copy_probe > 0:
@@ -394,6 +401,67 @@ def extras(wk, scores_h, bias_h, idx, wts, steps):
     return res
 
 
+def timing_protocol(step, stages, flush_bytes=1 << 30, replays=20):
+    """The step and each stage captured in HIP graphs and replayed: `replays`
+    times with a cold cache (a read of flush_bytes from a scratch buffer
+    before each replay, outside the timed events: more than the 256 MB
+    memory-side cache and the L2s together; a read, so that no write-back
+    of the flush itself overlaps the replay) and as many times warm; median
+    and minimum in microseconds. Also a plain device copy of flush_bytes as
+    the achievable-bandwidth probe (read + write bytes / time)."""
+    import torch
+    scratch = torch.ones(flush_bytes // 8, dtype=torch.int64, device="cuda:0")
+    sink = torch.empty((), dtype=torch.int64, device="cuda:0")
+
+    def capture(fn):
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            fn()
+        torch.cuda.current_stream().wait_stream(st)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        for _ in range(5):
+            g.replay()
+        torch.cuda.synchronize()
+        return g
+
+    def replay_times(g, cold):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(replays)]
+        for a, b in evs:
+            if cold:
+                torch.sum(scratch, dim=0, out=sink)
+            a.record()
+            g.replay()
+            b.record()
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+        return {"median_us": us[len(us) // 2], "min_us": us[0], "replays": replays}
+
+    res = {}
+    g = capture(step)
+    res["step_graph_cold"] = replay_times(g, True)
+    res["step_graph_warm"] = replay_times(g, False)
+    res["stage_graph_cold_median_us"] = {
+        name: replay_times(capture(fn), True)["median_us"] for name, fn in stages.items()}
+    dst = torch.empty_like(scratch)
+    dst.copy_(scratch)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(5):
+        dst.copy_(scratch)
+    b.record()
+    torch.cuda.synchronize()
+    res["copy_probe_gbps"] = 2 * flush_bytes * 5 / (a.elapsed_time(b) * 1e-3) / 1e9
+    del scratch, dst
+    return res
+
+
 def cpu_leg(wk, scores_h, bias_h, down, idx, wts, order, restore, starts, eids, stats, out,
             budget_s):
     """Time the CPU oracle over whole steps of the same workload and check the
@@ -435,6 +503,28 @@ def cpu_leg(wk, scores_h, bias_h, down, idx, wts, order, restore, starts, eids, 
                 "kind": "oracle",
                 "sample": "%d whole steps of the %s workload (router + create_indices + "
                           "finalize), %.1f s" % (steps, wk.name, el)}
+
+    # per stage, once each, on all threads and on one thread
+    def stage_times():
+        t = {}
+        a = time.perf_counter()
+        r_i, r_w = oracle.router(s, b, K, wk.n_groups, wk.topk_group, wk.norm_weights, wk.scale)
+        t["router"] = time.perf_counter() - a
+        a = time.perf_counter()
+        r_ind = oracle.create_indices(r_i, E)
+        t["create_indices"] = time.perf_counter() - a
+        a = time.perf_counter()
+        oracle.finalize(d, dcode, r_ind["restore_token_order"], r_w, oracle.F32, ocode)
+        t["finalize"] = time.perf_counter() - a
+        return {k: v * 1e3 for k, v in t.items()}
+
+    threads = oracle.num_threads()
+    baseline["stage_ms"] = stage_times()
+    oracle.set_num_threads(1)
+    try:
+        baseline["single_thread_stage_ms"] = stage_times()
+    finally:
+        oracle.set_num_threads(threads)
 
     u32 = lambda t: t.cpu().numpy().view(np.uint32)
     gi = idx.cpu().numpy()

@@ -84,6 +84,8 @@ def _load():
             getattr(lib, fn).restype = None
         lib.moe_oracle_num_threads.argtypes = []
         lib.moe_oracle_num_threads.restype = ctypes.c_int
+        lib.moe_oracle_set_num_threads.argtypes = [ctypes.c_int]
+        lib.moe_oracle_set_num_threads.restype = None
         _lib = lib
     return _lib
 
@@ -95,6 +97,12 @@ def _ptr(a: np.ndarray):
 def _check(rc: int, what: str):
     if rc != 0:
         raise ValueError("oracle %s: %s" % (what, _ERRORS.get(rc, "error %d" % rc)))
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the oracle's parallel loops use from now on (results do not
+    depend on it: the loops split whole tokens or chunks)."""
+    _load().moe_oracle_set_num_threads(int(n))
 
 
 def num_threads() -> int:

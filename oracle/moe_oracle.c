@@ -57,6 +57,15 @@ int moe_oracle_num_threads(void) {
 #endif
 }
 
+/* Threads for the following parallel loops (results do not depend on it). */
+void moe_oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------ */
 /* bfloat16 helpers                                                   */
 /* ------------------------------------------------------------------ */
