@@ -250,7 +250,9 @@ size_t moe_route_and_index_workspace_size(int64_t T, int32_t K, int32_t E);
  *                    call leaves it zero again (a buffer sized for the
  *                    largest batch serves every smaller one). Calls that
  *                    share a workspace must not run concurrently (one
- *                    stream, or ordered streams).
+ *                    stream, or ordered streams). A workspace that is not
+ *                    zero gives wrong index outputs but no access outside
+ *                    any buffer.
  *
  * Validation: that of the two separate calls, and the workspace size. With T = 0 only the index
  * metadata outputs are written, as moe_create_indices does for N = 0.
