@@ -3,6 +3,8 @@
 // mapping onto CDNA lanes are described in router.hip.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace moe {
@@ -200,7 +202,7 @@ __device__ __forceinline__ void route_tokens(
   const bool tok_ok = t < T;
   const int e0 = sub * EPL;
   const uint64_t segmask =
-      (LPT == kWave) ? ~0ull : (((1ull << LPT) - 1ull) << tok_lane0);
+      (LPT == kWave) ? ~0ull : (((1ull << (LPT & 63)) - 1ull) << tok_lane0);
 
   float s[EPL], bi[EPL], b[EPL];
   bool present[EPL];  // expert e0 + i exists (always, unless GEN)
@@ -331,25 +333,37 @@ __device__ __forceinline__ void route_tokens(
     pk[i] = (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(EPL - 1 - i);
   }
   sort_desc_u64<EPL>(pk);
+  // The sorted list as keys plus one word of 4-bit element indices (element
+  // of position i in bits 4i..4i+3): a pop shifts the keys by one register
+  // and the index word by 4 bits.
+  using IdxWord = typename std::conditional<(EPL > 8), uint64_t, uint32_t>::type;
+  uint32_t kv[EPL];
+  IdxWord iw = 0;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    kv[i] = static_cast<uint32_t>(pk[i] >> 32);
+    iw |= static_cast<IdxWord>((EPL - 1) - static_cast<uint32_t>(pk[i] & (EPL - 1))) << (4 * i);
+  }
 
   uint32_t my_id = 0;
   for (int k = 0; k < K; ++k) {
-    const uint32_t head = static_cast<uint32_t>(pk[0] >> 32);
+    const uint32_t head = kv[0];
     const uint64_t bal = __ballot(head == segment_max<LPT>(head)) & segmask;
     const int win = __builtin_ctzll(static_cast<unsigned long long>(bal));
-    uint32_t id;
     if constexpr (LPT == kWave) {
-      const uint32_t low = static_cast<uint32_t>(
-          __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(pk[0])), win));
-      id = static_cast<uint32_t>(win * EPL + (EPL - 1)) - (low & (EPL - 1));
+      // the winner and its element are wave-uniform; slot k lives in lane k
+      const uint32_t elem =
+          static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(iw & 0xFu), win));
+      const uint32_t id = static_cast<uint32_t>(win * EPL) + elem;
+      if (lane == k) my_id = id;
     } else {
-      id = static_cast<uint32_t>(win - tok_lane0);  // one expert per lane
+      if (sub == k) my_id = static_cast<uint32_t>(win - tok_lane0);  // one expert per lane
     }
-    if (sub == k) my_id = id;
     if (lane == win) {
 #pragma unroll
-      for (int i = 0; i + 1 < EPL; ++i) pk[i] = pk[i + 1];
-      pk[EPL - 1] = 0u;
+      for (int i = 0; i + 1 < EPL; ++i) kv[i] = kv[i + 1];
+      kv[EPL - 1] = 0u;
+      iw >>= 4;
     }
   }
 
