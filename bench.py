@@ -402,8 +402,9 @@ def extras(wk, scores_h, bias_h, idx, wts, steps):
 
 
 def timing_protocol(step, stages, flush_bytes=1 << 30, replays=20):
-    """The step and each stage captured in HIP graphs and replayed: `replays`
-    times with a cold cache (a read of flush_bytes from a scratch buffer
+    """The step and each stage captured in HIP graphs and replayed (one step
+    per graph, and 20 steps per graph for the GPU time per step with the
+    graph launch amortised): `replays` times with a cold cache (a read of flush_bytes from a scratch buffer
     before each replay, outside the timed events: more than the 256 MB
     memory-side cache and the L2s together; a read, so that no write-back
     of the flush itself overlaps the replay) and as many times warm; median
@@ -445,6 +446,17 @@ def timing_protocol(step, stages, flush_bytes=1 << 30, replays=20):
     g = capture(step)
     res["step_graph_cold"] = replay_times(g, True)
     res["step_graph_warm"] = replay_times(g, False)
+    # 20 steps per graph: the graph launch amortised, GPU time per step
+    many = 20
+
+    def steps():
+        for _ in range(many):
+            step()
+
+    g20 = capture(steps)
+    w20 = replay_times(g20, False)
+    res["steps_per_graph_20_warm_us_per_step"] = {"median": w20["median_us"] / many,
+                                                   "min": w20["min_us"] / many}
     res["stage_graph_cold_median_us"] = {
         name: replay_times(capture(fn), True)["median_us"] for name, fn in stages.items()}
     dst = torch.empty_like(scratch)
