@@ -39,6 +39,7 @@ import json
 import os
 import sys
 import time
+from dataclasses import replace
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -295,11 +296,10 @@ def extras(wk, scores_h, bias_h, idx, wts, steps):
       * router + index creation through the two entry points against
         moe_route_and_index (router filling the index histogram), same
         workload;
-      * the decode-shaped workload (T=128): whole steps (router ->
-        create_indices -> finalize) captured 20 to a HIP graph, mean GPU time
-        per step (eager launches would measure the host, not the GPU); the
-        same with router and index creation fused into one launch; and
-        router + index creation alone, separate and fused."""
+      * the decode-shaped workload (T=128, and T=16, which
+        moe_route_and_index routes in one launch): whole steps captured 20
+        to a HIP graph (decode_latency; eager launches would measure the
+        host, not the GPU)."""
     import torch
 
     from permutation_group_limited_amd import binding
@@ -352,6 +352,23 @@ def extras(wk, scores_h, bias_h, idx, wts, steps):
         wk.norm_weights, wk.scale))
 
     dk = wl.WORKLOADS["decode"]
+    res["decode"] = decode_latency(dk)
+    # a batch small enough for moe_route_and_index's one-launch form
+    res["decode_t16"] = decode_latency(replace(dk, T=16))
+    return res
+
+
+def decode_latency(dk):
+    """Decode-sized steps (router -> create_indices -> finalize) captured 20
+    to a HIP graph: mean GPU time per step through the separate entry points
+    and with moe_route_and_index, and router + index creation alone both
+    ways."""
+    import torch
+
+    from permutation_group_limited_amd import binding
+    from permutation_group_limited_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
     T, E, K = dk.T, dk.E, dk.K
     s = wl.make_scores(dk).to(dev)
     b = wl.make_bias(dk).to(dev)
@@ -391,14 +408,13 @@ def extras(wk, scores_h, bias_h, idx, wts, steps):
         dk.scale))
     db = T * E * 4 + E * 4 + T * K * 8 + T * K * 12 + (2 * E + 1) * 4 + 8 + \
         T * K * dk.H * 2 + T * K * 8 + T * dk.H * 2
-    res["decode"] = {"workload": dk.describe(), "us_per_step_graph": us,
-                     "us_per_step_graph_fused": us_fused,
-                     "us_route_index_graph": us_ri_sep,
-                     "us_route_index_graph_fused": us_ri_fused,
-                     "token_slots_per_s": T * K / (us * 1e-6),
-                     "token_slots_per_s_fused": T * K / (us_fused * 1e-6),
-                     "hbm_gbps": db / (us * 1e-6) / 1e9}
-    return res
+    return {"workload": dk.describe(), "us_per_step_graph": us,
+            "us_per_step_graph_fused": us_fused,
+            "us_route_index_graph": us_ri_sep,
+            "us_route_index_graph_fused": us_ri_fused,
+            "token_slots_per_s": T * K / (us * 1e-6),
+            "token_slots_per_s_fused": T * K / (us_fused * 1e-6),
+            "hbm_gbps": db / (us * 1e-6) / 1e9}
 
 
 def timing_protocol(step, stages, flush_bytes=1 << 30, replays=20):

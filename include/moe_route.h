@@ -225,8 +225,10 @@ size_t moe_route_and_index_workspace_size(int64_t T, int32_t K, int32_t E);
  * moe_create_indices on its expert_indices, with fewer launches. Every
  * output is bit-identical to what the two separate calls produce on the
  * same inputs.
- *   - E a power of two and T * K <= 16384: one launch (the last workgroup
- *     to finish routing builds the index outputs);
+ *   - E a power of two and T no larger than one router workgroup's share
+ *     (16 tokens for E in 64..256, 8 for 512, 4 for 1024, 64 * 16 / E
+ *     below 64): one launch, that workgroup routing every token and then
+ *     building the index outputs;
  *   - otherwise two launches: the router also counts each chunk's slots per
  *     expert (relaxed atomic adds into the workspace's counts matrix), so
  *     the index step needs no histogram pass of its own; its last

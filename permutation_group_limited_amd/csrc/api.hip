@@ -223,13 +223,13 @@ moe_status_t moe_route_and_index(int32_t* expert_indices, void* expert_weights,
     return launch_indices(token_expert_order, expert_start_indices, restore_token_order,
                           expert_ids, expert_usage_stats, scales_offset, scale_align,
                           expert_indices, 0, E, nullptr, plan, false, nullptr, s);
-  if (is_pow2(E) && N <= kRouteIndexMaxSlots)  // one launch
+  if (T <= route_index_max_tokens(E))  // one workgroup routes it all: one launch
     return launch_route_index(expert_indices, expert_weights, router_input, expert_bias,
                               input_dtype, bias_dtype, static_cast<int32_t>(score_fn), T, E, K,
                               n_groups, topk_group, norm_weights ? 1 : 0, routed_scaling_factor,
                               static_cast<int32_t>(group_score), token_expert_order,
                               expert_start_indices, restore_token_order, expert_ids,
-                              expert_usage_stats, scales_offset, scale_align, ticket, s);
+                              expert_usage_stats, scales_offset, scale_align, s);
   // two launches: the router also fills the index step's counts matrix,
   // then the scatter (which clears the matrix again) takes no histogram pass
   const bool multi = plan.nchunks > 1;

@@ -157,19 +157,16 @@ moe_status_t launch_indices(uint32_t* token_expert_order, uint32_t* expert_start
                             void* workspace, const IndexPlan& plan, bool counts_ready,
                             uint32_t* ticket, hipStream_t stream);
 
-// Router and index creation in one launch: every workgroup routes its
-// tokens, then the last one to finish (counted on `ticket`, one uint32 that
-// must be zero on entry and is left zero) builds all index outputs from the
-// expert_indices just written, as one chunk. For small T * K (decode).
-constexpr int64_t kRouteIndexMaxSlots = 16384;
+// Router and index creation in one launch, for batches that one workgroup
+// routes alone (T <= route_index_max_tokens(E)).
+int64_t route_index_max_tokens(int32_t E);
 moe_status_t launch_route_index(int32_t* idx, void* w, const void* s, const void* b,
                                 moe_dtype_t sd, moe_dtype_t bd, int32_t fn, int64_t T, int32_t E,
                                 int32_t K, int32_t G, int32_t TG, int32_t norm, float scale,
                                 int32_t mode, uint32_t* token_expert_order,
                                 uint32_t* expert_start_indices, uint32_t* restore_token_order,
                                 int32_t* expert_ids, uint32_t* expert_usage_stats,
-                                uint32_t* scales_offset, uint32_t scale_align, uint32_t* ticket,
-                                hipStream_t stream);
+                                uint32_t* scales_offset, uint32_t scale_align, hipStream_t stream);
 
 moe_status_t launch_finalize(void* output, moe_dtype_t out_dtype, const void* down,
                              moe_dtype_t down_dtype, const uint32_t* restore_order,

@@ -1,5 +1,5 @@
-// Router and index creation in one launch: dtype dispatch. The kernel and
-// the hand-over between its two stages are in route_index_impl.hpp.
+// Router and index creation in one launch (single-workgroup batches): dtype
+// dispatch and the batch limit. The kernel is in route_index_impl.hpp.
 #include "route_index.hpp"
 
 namespace moe {
@@ -10,13 +10,13 @@ moe_status_t launch_route_index(int32_t* idx, void* w, const void* s, const void
                                 int32_t mode, uint32_t* token_expert_order,
                                 uint32_t* expert_start_indices, uint32_t* restore_token_order,
                                 int32_t* expert_ids, uint32_t* expert_usage_stats,
-                                uint32_t* scales_offset, uint32_t scale_align, uint32_t* ticket,
+                                uint32_t* scales_offset, uint32_t scale_align,
                                 hipStream_t stream) {
   const IndexOutputs io{token_expert_order, expert_start_indices, restore_token_order,
                         expert_ids, expert_usage_stats, scales_offset, scale_align};
 #define MOE_D(DS, DB)                                                                        \
   return launch_route_index_dt<DS, DB>(fn, E, idx, w, s, b, T, K, G, TG, norm, scale, mode, io, \
-                                       ticket, stream)
+                                       stream)
   if (sd == MOE_DTYPE_F32 && bd == MOE_DTYPE_F32) MOE_D(DF32, DF32);
   if (sd == MOE_DTYPE_BF16 && bd == MOE_DTYPE_BF16) MOE_D(DBF16, DBF16);
   if (sd == MOE_DTYPE_BF16 && bd == MOE_DTYPE_F32) MOE_D(DBF16, DF32);
@@ -24,6 +24,14 @@ moe_status_t launch_route_index(int32_t* idx, void* w, const void* s, const void
   if (sd == MOE_DTYPE_F16 && bd == MOE_DTYPE_F32) MOE_D(DF16, DF32);
 #undef MOE_D
   return MOE_ERR_UNSUPPORTED;
+}
+
+int64_t route_index_max_tokens(int32_t E) {
+  // W * (64 / LPT) with W = min(16, 4096 / E) waves and LPT = min(E, 64)
+  if (E < 1 || E > 1024 || (E & (E - 1)) != 0) return 0;
+  const int64_t waves = E <= 256 ? 16 : 4096 / E;
+  const int64_t lanes_per_token = E < kWave ? E : kWave;
+  return waves * (kWave / lanes_per_token);
 }
 
 }  // namespace moe

@@ -1,6 +1,6 @@
-// Router + index creation in one launch: the per-dtype instance sets, each
-// compiled in a translation unit of its own (route_index_*.hip) so that the
-// many instances build in parallel.
+// Router + index creation in one launch (single-workgroup batches): the
+// per-dtype instance sets, each compiled in a translation unit of its own
+// (route_index_*.hip) so that the many instances build in parallel.
 #pragma once
 
 #include "common.hpp"
@@ -22,6 +22,10 @@ template <typename DS, typename DB>
 moe_status_t launch_route_index_dt(int32_t fn, int32_t E, int32_t* idx, void* w, const void* s,
                                    const void* b, int64_t T, int32_t K, int32_t G, int32_t TG,
                                    int32_t norm, float scale, int32_t mode, IndexOutputs io,
-                                   uint32_t* ticket, hipStream_t stream);
+                                   hipStream_t stream);
+
+// Largest T that one workgroup routes for E experts (0: no one-launch form,
+// E not a power of two or above 1024).
+int64_t route_index_max_tokens(int32_t E);
 
 }  // namespace moe

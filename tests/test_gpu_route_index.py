@@ -1,12 +1,15 @@
 """GPU parity of moe_route_and_index (router and index creation with fewer
-launches: one for small power-of-two-E batches, else the router filling the
-index step's histogram, then the scatter) against the oracle's router
+launches: one when a single workgroup routes the whole batch, e.g. T <= 16
+at E = 256, else the router filling the index step's histogram, then the
+scatter) against the oracle's router
 followed by its index creation, and bit-identity with the two separate GPU
 entry points on the same inputs; the workspace is all zero after each call.
 
 Acceptance as for the separate stages: indices and every index output
 bit-exact; fp32 weights within 1e-6 relative, 16-bit weights within 1 ulp
 of the oracle and bit-identical to the separate router call. Marked gpu."""
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -149,11 +152,20 @@ def test_workload_shapes(name, T, from_logits):
     check_same(got, separate(x, b, *args))
 
 
-@pytest.mark.parametrize("T,E,G,TG,K", [(1, 1, 1, 1, 1), (33, 2, 1, 1, 2), (129, 8, 4, 2, 3),
-                                        (300, 32, 8, 4, 6), (77, 64, 8, 3, 6),
-                                        (511, 128, 8, 4, 8), (1000, 256, 8, 4, 8),
-                                        (61, 512, 16, 4, 8), (2048, 1024, 16, 4, 8),
-                                        # two launches: several chunks, or E not a power of two
+@pytest.mark.parametrize("T,E,G,TG,K", [# one launch: a single workgroup routes every token
+                                        (1, 1, 1, 1, 1), (1024, 1, 1, 1, 1), (33, 2, 1, 1, 2),
+                                        (512, 2, 1, 1, 2), (128, 8, 4, 2, 3), (127, 8, 4, 2, 4),
+                                        (32, 32, 8, 4, 6), (16, 64, 8, 3, 6), (16, 128, 8, 4, 8),
+                                        (16, 256, 8, 4, 8), (9, 256, 8, 4, 8), (8, 512, 16, 4, 8),
+                                        (4, 1024, 16, 4, 8), (3, 1024, 16, 4, 8),
+                                        # two launches: one chunk or several, E a power of two
+                                        # or not, just above the one-launch limits included
+                                        (1025, 1, 1, 1, 1), (129, 8, 4, 2, 3), (33, 32, 8, 4, 6),
+                                        (17, 256, 8, 4, 8), (9, 512, 16, 4, 8),
+                                        (5, 1024, 16, 4, 8), (300, 32, 8, 4, 6),
+                                        (77, 64, 8, 3, 6), (511, 128, 8, 4, 8),
+                                        (1000, 256, 8, 4, 8), (61, 512, 16, 4, 8),
+                                        (2048, 1024, 16, 4, 8),
                                         (5000, 1024, 16, 4, 8), (2500, 8, 1, 1, 8),
                                         (100, 160, 8, 3, 6), (4096, 160, 8, 3, 6),
                                         (777, 20, 4, 3, 6), (3000, 1000, 8, 4, 8)])
@@ -229,12 +241,17 @@ def test_back_to_back_calls_share_the_counter():
         check_against_oracle(o.host(), x, b, wk.K, 8, 4, True, 2.5)
 
 
-@pytest.mark.parametrize("name", ["decode", "dsv3"])
-def test_graph_replay(name):
+@pytest.mark.parametrize("name,T", [("tiny", None), ("decode", 16), ("decode", None),
+                                    ("dsv3", None)])
+def test_graph_replay(name, T):
     """Captured once, replayed several times with eager work in between;
-    every replay gives the eager result and leaves the workspace zero."""
+    every replay gives the eager result and leaves the workspace zero (the
+    one-launch form at T = 64, E = 8 and T = 16, E = 256, the two-launch
+    form with one chunk and with several)."""
     wk = wl.WORKLOADS[name]
-    log("route_and_index graph replay", name)
+    if T is not None:
+        wk = replace(wk, T=T)
+    log("route_and_index graph replay", wk.describe())
     x = wl.make_scores(wk).to(DEV)
     b = wl.make_bias(wk).to(DEV)
     ws = workspace(wk.T, wk.K, wk.E)
