@@ -180,7 +180,7 @@ moe_status_t moe_create_indices_aligned(uint32_t* token_expert_order,
 static constexpr size_t kTicketBytes = 256;
 
 static size_t route_index_workspace(int64_t N, int32_t E) {
-  const IndexPlan plan = plan_indices(N, E);
+  const IndexPlan plan = plan_indices(N, E, true);
   return kTicketBytes + (plan.nchunks > 1 ? plan.workspace_bytes : 0);
 }
 
@@ -218,7 +218,7 @@ moe_status_t moe_route_and_index(int32_t* expert_indices, void* expert_weights,
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint32_t* ticket = static_cast<uint32_t*>(workspace);
   uint32_t* counts = ticket + kTicketBytes / sizeof(uint32_t);
-  const IndexPlan plan = plan_indices(N, E);
+  const IndexPlan plan = plan_indices(N, E, true);
   if (T == 0)  // nothing to route: the index step alone writes the metadata
     return launch_indices(token_expert_order, expert_start_indices, restore_token_order,
                           expert_ids, expert_usage_stats, scales_offset, scale_align,

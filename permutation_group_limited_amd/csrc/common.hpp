@@ -143,7 +143,9 @@ struct IndexPlan {
   int rounds;       // 64-slot rounds per wave
   size_t workspace_bytes;
 };
-IndexPlan plan_indices(int64_t N, int32_t E);
+// router_counts: the plan of moe_route_and_index's two-launch form, where
+// the router fills the counts matrix.
+IndexPlan plan_indices(int64_t N, int32_t E, bool router_counts = false);
 
 // scales_offset may be NULL (then scale_align is ignored). With
 // counts_ready the counts matrix in `workspace` was already filled (by the

@@ -92,6 +92,12 @@ def test_workspace_size(lib):
     big = lib.moe_create_indices_workspace_size(524288, 256)
     assert big >= 256 * 4 and big % 4 == 0
     assert lib.moe_create_indices_workspace_size(-1, 256) == 0
+    # one workgroup (no workspace) up to 5 rounds of 1024 slots; 8 rounds for
+    # E <= 16 and for E > 256 (rounds of 256 slots)
+    ws = lib.moe_create_indices_workspace_size
+    assert ws(5120, 256) == 0 and ws(5121, 256) == 256 * 4 * 6
+    assert ws(8192, 8) == 0 and ws(8193, 8) == 8 * 4 * 9
+    assert ws(2048, 512) == 0 and ws(2049, 512) == 512 * 4 * 9
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -172,6 +178,10 @@ def test_route_and_index_workspace_size(lib):
     assert ws(8192, 8, 256) == 256 + lib.moe_create_indices_workspace_size(65536, 256)
     assert ws(8192, 8, 256) > 256
     assert ws(100, 6, 160) == 256
+    # after the router has counted: one workgroup up to 4 rounds of 1024 slots
+    assert ws(512, 8, 256) == 256 and ws(513, 8, 256) == 256 + 256 * 4 * 5
+    assert ws(2048, 2, 8) == 256 and ws(2049, 2, 8) == 256 + 8 * 4 * 5
+    assert ws(256, 8, 512) == 256 and ws(257, 8, 512) == 256 + 512 * 4 * 9
     assert ws(-1, 8, 256) == 0 and ws(8, 0, 256) == 0 and ws(8, 8, 2048) == 0
 
 
