@@ -156,3 +156,56 @@ def test_huge_n_properties(N, E):
     exp_ids[:A] = active
     assert torch.equal(eids.long(), exp_ids)
     assert stats.tolist() == [int(cnt.max()), A]
+
+
+def test_max_n_properties():
+    """The largest problem the uint32 outputs allow: N = 2^32 - 1 slots over
+    E = 256 (16 GiB per [N] array). Same defining properties as above,
+    checked in slices of 2^28 slots on the GPU, with uint32 values read
+    through int64 (positions above 2^31 - 1 are negative as int32)."""
+    N, E = (1 << 32) - 1, 256
+    log("indices max N", N, "E", E)
+    dev = "cuda:0"
+    g = torch.Generator(device=dev).manual_seed(5)
+    ids = torch.randint(0, E, (N,), generator=g, dtype=torch.int32, device=dev)
+    order = torch.full((N,), -1, dtype=torch.int32, device=dev)
+    restore = torch.full((N,), -1, dtype=torch.int32, device=dev)
+    starts = torch.full((E + 1,), -1, dtype=torch.int32, device=dev)
+    eids = torch.full((E,), -7, dtype=torch.int32, device=dev)
+    stats = torch.full((2,), -1, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(binding.moe_create_indices_workspace_size(N, E), 4) // 4,
+                     dtype=torch.int32, device=dev)
+    binding.moe_create_indices(order, starts, restore, eids, stats, ids, ws)
+    torch.cuda.synchronize()
+    log("indices max N: kernels done, checking")
+    u32 = lambda t: t.long() & 0xFFFFFFFF  # noqa: E731
+    cnt = torch.zeros(E, dtype=torch.long, device=dev)
+    step = 1 << 28
+    prev_id, prev_slot = -1, -1
+    for a in range(0, N, step):
+        b = min(a + step, N)
+        o = u32(order[a:b])
+        assert int(o.max()) < N
+        # restore(order(i)) == i for every i makes order injective, hence a
+        # permutation of [0, N), and restore its inverse
+        assert torch.equal(u32(restore[o]), torch.arange(a, b, device=dev))
+        seg = ids[o].long()
+        assert int(seg[0]) >= prev_id and (int(seg[0]) > prev_id or int(o[0]) > prev_slot)
+        assert bool((seg[1:] >= seg[:-1]).all())
+        same = seg[1:] == seg[:-1]
+        assert bool((o[1:] > o[:-1])[same].all())
+        prev_id, prev_slot = int(seg[-1]), int(o[-1])
+        cnt += torch.bincount(ids[a:b].long(), minlength=E)
+        del o, seg, same
+    active = torch.nonzero(cnt).flatten()
+    A = active.numel()
+    csum = torch.cat([torch.zeros(1, dtype=torch.long, device=dev), torch.cumsum(cnt, 0)])
+    exp_starts = torch.full((E + 1,), N, dtype=torch.long, device=dev)
+    exp_starts[:A] = csum[active]
+    assert torch.equal(u32(starts), exp_starts)
+    exp_ids = torch.full((E,), -1, dtype=torch.long, device=dev)
+    exp_ids[:A] = active
+    assert torch.equal(eids.long(), exp_ids)
+    assert u32(stats).tolist() == [int(cnt.max()), A]
+    del ids, order, restore
+    torch.cuda.empty_cache()

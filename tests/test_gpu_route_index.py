@@ -279,3 +279,30 @@ def test_graph_replay(name, T):
         torch.cuda.synchronize()
         assert_zero(ws, "after replay %d" % rep)
         check_same(o.host(), ref)
+
+
+def test_huge_batch_matches_separate():
+    """2^22 + 3 tokens of the DSv3 shape (4 GiB of scores; 33.5M slots in 64
+    index chunks): every output equal, bit for bit and compared on the GPU,
+    to the two separate entry points (whose own parity at this size is
+    covered by the sampled router test and the index-property tests), and
+    the workspace left zero."""
+    T, E, K, G, TG = (1 << 22) + 3, 256, 8, 8, 4
+    log("route_and_index huge batch", T)
+    g = torch.Generator(device=DEV).manual_seed(21)
+    x = torch.sigmoid(torch.randn(T, E, generator=g, device=DEV))
+    b = wl.random_bias(E, seed=22).to(DEV)
+    ws = workspace(T, K, E)
+    fo = Outputs(T, E, K, torch.float32, True)
+    launch(fo, x, b, ws, G, TG, True, 2.5, binding.SCORE_NONE, align=16)
+    so = Outputs(T, E, K, torch.float32, True)
+    binding.moe_router_group_limited(so.idx, so.w, x, b, G, TG, True, 2.5)
+    n = binding.moe_create_indices_workspace_size(T * K, E)
+    ws2 = torch.empty(max(n, 4) // 4, dtype=torch.int32, device=DEV)
+    binding.moe_create_indices_aligned(so.order, so.starts, so.restore, so.eids, so.stats,
+                                       so.idx, ws2, so.scales, 16)
+    torch.cuda.synchronize()
+    assert_zero(ws)
+    for name in ("idx", "order", "restore", "starts", "eids", "stats", "scales"):
+        assert torch.equal(getattr(fo, name), getattr(so, name)), name
+    assert torch.equal(fo.w.view(torch.int32), so.w.view(torch.int32))

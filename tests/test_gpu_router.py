@@ -165,10 +165,11 @@ def test_logits_random_shapes(fn, T, E, G, TG, K, dt):
 
 
 def test_huge_batch_sampled():
-    """2^20 + 3 tokens of the DSv3 shape (1 GiB of scores), routed in one
-    call; each token's result depends on its own row only, so the oracle
-    checks 4,099 of them (random rows, the first and the last)."""
-    T, E, K, G, TG = (1 << 20) + 3, 256, 8, 8, 4
+    """2^22 + 3 tokens of the DSv3 shape (4 GiB of scores, so byte offsets
+    past 2^32), routed in one call; each token's result depends on its own
+    row only, so the oracle checks 4,099 of them (random rows, the first and
+    the last)."""
+    T, E, K, G, TG = (1 << 22) + 3, 256, 8, 8, 4
     log("router huge batch", T)
     dev = "cuda:0"
     g = torch.Generator(device=dev).manual_seed(11)
