@@ -289,7 +289,8 @@ moe_status_t moe_route_and_index(int32_t* expert_indices, void* expert_weights,
  * conversion to bf16 / fp16 rounds to nearest even.
  *
  * Validation: T >= 0, K >= 1, H >= 0, T*K < 2^32; dtypes in {F32, BF16,
- * F16}, any combination; an output row below 2^31 bytes (larger:
+ * F16}, any combination; an output row below 2^31 bytes and
+ * T * ceil(H * sizeof(down_dtype) / 1024) below 2^32 - 2^18 (larger:
  * MOE_ERR_UNSUPPORTED); H * sizeof(down_dtype) a multiple of 16 bytes;
  * output and down 16-byte aligned; non-NULL pointers when T*H > 0.
  * Precondition: restore_order[i] < T*K (an out-of-range entry contributes

@@ -101,6 +101,23 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
 
 __device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x) & (kWave - 1); }
 
+// A grid holds at most 2^32 - 1 work-items per dimension. A 1-D problem
+// needing more (e.g. the router at 2^26 tokens of 64 lanes each) is laid
+// out as rows of kGridRow workgroups along y; kernels take the linear
+// workgroup index below and skip the padding workgroups of the last row.
+constexpr uint32_t kGridRow = 1u << 16;
+
+inline dim3 grid_1d(int64_t blocks, int threads_per_block) {
+  if (blocks * threads_per_block <= static_cast<int64_t>(UINT32_MAX))
+    return dim3(static_cast<uint32_t>(blocks));
+  return dim3(kGridRow, static_cast<uint32_t>((blocks + kGridRow - 1) / kGridRow));
+}
+
+// Linear workgroup index (fewer than 2^32 workgroups per launch).
+__device__ __forceinline__ uint32_t linear_block() {
+  return blockIdx.x + blockIdx.y * gridDim.x;
+}
+
 // Number of set bits of `mask` in lanes below the calling lane.
 __device__ __forceinline__ uint32_t popc_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),

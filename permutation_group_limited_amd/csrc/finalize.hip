@@ -83,8 +83,9 @@ __global__ __launch_bounds__(kBlock) void finalize_kernel(
     int64_t T, int32_t K, int64_t H, int32_t chunks_per_row, uint32_t n_rows) {
   constexpr int VEC = 16 / DD::kBytes;  // elements per 16-byte load
   const int lane = lane_id();
-  // the host keeps T * chunks_per_row below 2^32, so 32-bit scalar math
-  const uint32_t gw = blockIdx.x * kWavesPerBlock +
+  // the host keeps T * chunks_per_row below 2^32, so 32-bit scalar math;
+  // grid padding (t >= T) returns below
+  const uint32_t gw = linear_block() * kWavesPerBlock +
                       __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(threadIdx.x) / kWave);
   const uint32_t cpr = static_cast<uint32_t>(chunks_per_row);
   const int64_t t = gw / cpr;
@@ -151,12 +152,14 @@ moe_status_t launch_typed(void* out, const void* down, const uint32_t* restore,
   const int64_t per_wave = static_cast<int64_t>(kWave) * VEC;
   const int64_t cpr = (H + per_wave - 1) / per_wave;
   const int64_t waves = T * cpr;
-  if (waves > 0xFFFFFFFFll - kWavesPerBlock) return MOE_ERR_UNSUPPORTED;
+  // wave indices (grid padding included) stay below 2^32
+  if (waves > 0xFFFFFFFFll - static_cast<int64_t>(kGridRow) * kWavesPerBlock)
+    return MOE_ERR_UNSUPPORTED;
   const int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
   const uint32_t n_rows = static_cast<uint32_t>(T * K);
   auto* o = static_cast<typename DO::storage*>(out);
   const auto* d = static_cast<const typename DD::storage*>(down);
-  const dim3 grid(static_cast<uint32_t>(blocks)), block(kBlock);
+  const dim3 grid = grid_1d(blocks, kBlock), block(kBlock);
   const int32_t c = static_cast<int32_t>(cpr);
 #define MOE_FIN(KB, EXACT)                                                                  \
   hipLaunchKernelGGL((finalize_kernel<DD, DO, KB, EXACT>), grid, block, 0, stream, o, d, \

@@ -38,7 +38,7 @@ __global__ __launch_bounds__(route_index_waves<EPL * LPT>() * kWave) void route_
   constexpr int E = EPL * LPT;
   constexpr int W = route_index_waves<E>();
   route_tokens<DS, DB, EPL, LPT, FN, W>(out_idx, out_w, scores, bias, T, K, n_groups, topk_group,
-                                        norm_weights, scale, mode);
+                                        norm_weights, scale, mode, 0u);
   __syncthreads();
   const int64_t N = T * K;
   scatter_chunk<W>(io.order, io.starts, io.restore, io.expert_ids, io.stats, io.scales_offset,

@@ -37,8 +37,8 @@ __global__ __launch_bounds__(kBlock) void router_kernel(
     int64_t T, int32_t K, int32_t n_groups, int32_t topk_group, int32_t norm_weights,
     float scale, int32_t mode, RouterHist hist) {
   route_tokens<DS, DB, EPL, LPT, FN, kWavesPerBlock>(out_idx, out_w, scores, bias, T, K, n_groups,
-                                                     topk_group, norm_weights, scale, mode, 0,
-                                                     hist);
+                                                     topk_group, norm_weights, scale, mode,
+                                                     linear_block(), 0, hist);
 }
 
 template <typename DS, typename DB, int EPL, int LPT, int FN>
@@ -48,7 +48,7 @@ struct RouterLaunch {
                           int32_t mode, RouterHist hist, hipStream_t stream) {
     constexpr int TPB = kWavesPerBlock * (kWave / LPT);  // tokens per block
     const int64_t blocks = (T + TPB - 1) / TPB;
-    hipLaunchKernelGGL((router_kernel<DS, DB, EPL, LPT, FN>), dim3(static_cast<uint32_t>(blocks)),
+    hipLaunchKernelGGL((router_kernel<DS, DB, EPL, LPT, FN>), grid_1d(blocks, kBlock),
                        dim3(kBlock), 0, stream, idx, static_cast<typename DS::storage*>(w),
                        static_cast<const typename DS::storage*>(s),
                        static_cast<const typename DB::storage*>(b), T, K, G, TG, norm, scale,
@@ -66,8 +66,8 @@ __global__ __launch_bounds__(kBlock) void router_any_e_kernel(
     int64_t T, int32_t K, int32_t n_groups, int32_t topk_group, int32_t norm_weights,
     float scale, int32_t mode, int32_t E, RouterHist hist) {
   route_tokens<DS, DB, EPL, kWave, FN, kWavesPerBlock, true>(
-      out_idx, out_w, scores, bias, T, K, n_groups, topk_group, norm_weights, scale, mode, E,
-      hist);
+      out_idx, out_w, scores, bias, T, K, n_groups, topk_group, norm_weights, scale, mode,
+      linear_block(), E, hist);
 }
 
 // Reached through dispatch_router with the padded expert count
@@ -81,8 +81,8 @@ struct RouterAnyELaunch {
       return MOE_ERR_UNSUPPORTED;
     } else {
       const int64_t blocks = (T + kWavesPerBlock - 1) / kWavesPerBlock;
-      hipLaunchKernelGGL((router_any_e_kernel<DS, DB, EPL, FN>),
-                         dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, stream, idx,
+      hipLaunchKernelGGL((router_any_e_kernel<DS, DB, EPL, FN>), grid_1d(blocks, kBlock),
+                         dim3(kBlock), 0, stream, idx,
                          static_cast<typename DS::storage*>(w),
                          static_cast<const typename DS::storage*>(s),
                          static_cast<const typename DB::storage*>(b), T, K, G, TG, norm, scale,

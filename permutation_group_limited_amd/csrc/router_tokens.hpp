@@ -175,8 +175,9 @@ __device__ __forceinline__ double segment_sum_f64(double v) {
   return v;
 }
 
-// Routes the tokens of workgroup blockIdx.x (WPB waves of kWave / LPT
-// tokens each) and writes their expert_indices and expert_weights rows.
+// Routes the tokens of workgroup `block` (WPB waves of kWave / LPT tokens
+// each) and writes their expert_indices and expert_weights rows. A
+// workgroup past the last token (grid padding) returns at once.
 //
 // GEN = false: E = EPL * LPT, a power of two, and groups of S = E / n_groups
 // experts cover whole lanes (S >= EPL), so the group stage is a lane
@@ -189,16 +190,18 @@ __device__ __forceinline__ void route_tokens(
     int32_t* __restrict__ out_idx, typename DS::storage* __restrict__ out_w,
     const typename DS::storage* __restrict__ scores, const typename DB::storage* __restrict__ bias,
     int64_t T, int32_t K, int32_t n_groups, int32_t topk_group, int32_t norm_weights,
-    float scale, int32_t mode, int32_t E_rt = 0, RouterHist hist = RouterHist{nullptr, 0u}) {
+    float scale, int32_t mode, uint32_t block, int32_t E_rt = 0,
+    RouterHist hist = RouterHist{nullptr, 0u}) {
   static_assert(!GEN || LPT == kWave, "the general-E form routes one token per wave");
   const int32_t E = GEN ? E_rt : EPL * LPT;
   constexpr int TPW = kWave / LPT;  // tokens per wave
+  const int64_t t0 = static_cast<int64_t>(block) * WPB * TPW;  // first token
+  if (t0 >= T) return;  // uniform over the workgroup, before any barrier
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
   const int sub = lane & (LPT - 1);
   const int tok_lane0 = lane & ~(LPT - 1);
-  const int64_t t =
-      (static_cast<int64_t>(blockIdx.x) * WPB + wave) * TPW + lane / LPT;
+  const int64_t t = t0 + static_cast<int64_t>(wave) * TPW + lane / LPT;
   const bool tok_ok = t < T;
   const int e0 = sub * EPL;
   const uint64_t segmask =
@@ -410,7 +413,6 @@ __device__ __forceinline__ void route_tokens(
   if (hist.counts != nullptr) {  // uniform
     constexpr int kThreads = WPB * kWave;
     __shared__ uint32_t keys[kThreads];
-    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * WPB * TPW;  // first token
     const int64_t t1 = (t0 + WPB * TPW < T) ? t0 + WPB * TPW : T;
     const int nslots = static_cast<int>((t1 - t0) * K);
     const uint32_t c0 = static_cast<uint32_t>((t0 * K) / hist.chunk);

@@ -6,6 +6,7 @@ import pytest
 import torch
 
 import oracle
+from permutation_group_limited_amd import binding
 from permutation_group_limited_amd import workloads as wl
 
 from _gpu import (DEV, assert_finalize_close, gpu_finalize, log, oracle_finalize_from,
@@ -94,3 +95,31 @@ def test_deterministic():
     for _ in range(3):
         assert torch.equal(gpu_finalize(dd, restore, w, torch.bfloat16).cpu().view(torch.int16),
                            a.view(torch.int16))
+
+
+def test_more_than_2_32_work_items():
+    """2^26 + 5 tokens, K = 1, H = 8 (one wave per token): more work-items
+    than one grid dimension holds, so the launch is laid out as rows of
+    workgroups. Sampled tokens (first, last, around 2^26, 4,096 random)
+    against the oracle; every output row written."""
+    T, K, H = (1 << 26) + 5, 1, 8
+    log("finalize 2-D grid", T)
+    dev = "cuda:0"
+    g = torch.Generator(device=dev).manual_seed(3)
+    down = torch.randn(T * K, H, generator=g, device=dev).to(torch.bfloat16)
+    w = torch.rand(T, K, generator=g, device=dev) * 2.0
+    restore = torch.randperm(T * K, generator=g, device=dev).to(torch.int32)
+    out = torch.full((T, H), float("nan"), dtype=torch.bfloat16, device=dev)
+    binding.moe_finalize(out, down, restore, w)
+    torch.cuda.synchronize()
+    assert not bool(torch.isnan(out).any())
+    ts = torch.randperm(T, generator=torch.Generator().manual_seed(4))[:4096]
+    edge = torch.tensor([0, 1, (1 << 26) - 1, 1 << 26, (1 << 26) + 1, T - 2, T - 1])
+    ts = torch.sort(torch.cat([ts, edge])).values.to(dev)
+    rows = restore.view(T, K)[ts].reshape(-1).long()
+    sub_down = down[rows].cpu()
+    exp = oracle_finalize_from(sub_down, np.arange(rows.numel(), dtype=np.uint32),
+                               w[ts].cpu(), torch.bfloat16)
+    assert_finalize_close(out[ts], exp, None)
+    del down, out, restore
+    torch.cuda.empty_cache()

@@ -184,3 +184,31 @@ def test_huge_batch_sampled():
     oi, ow = oracle.router(s[rows].cpu().numpy(), b.cpu().numpy(), K, G, TG, True, 2.5)
     assert np.array_equal(idx[rows].cpu().numpy(), oi)
     assert_weights_close(w[rows].cpu().numpy(), ow)
+
+
+@pytest.mark.parametrize("E,G,TG,K", [(64, 8, 4, 8), (96, 8, 4, 8)])
+def test_more_than_2_32_work_items(E, G, TG, K):
+    """2^26 + 5 tokens of 64 lanes each: more work-items than one grid
+    dimension holds, so the launch is laid out as rows of workgroups (the
+    power-of-two form at E = 64, the general form at E = 96). Sampled
+    tokens against the oracle: the first and last, those around token 2^26
+    and 4,096 random ones."""
+    T = (1 << 26) + 5
+    log("router 2-D grid", T, "E", E)
+    dev = "cuda:0"
+    g = torch.Generator(device=dev).manual_seed(E)
+    s = torch.rand(T, E, generator=g, device=dev)
+    b = wl.random_bias(E, seed=E + 1).to(dev)
+    idx = torch.full((T, K), -7, dtype=torch.int32, device=dev)
+    w = torch.full((T, K), float("nan"), device=dev)
+    binding.moe_router_group_limited(idx, w, s, b, G, TG, True, 2.5)
+    torch.cuda.synchronize()
+    rows = torch.randperm(T, generator=torch.Generator().manual_seed(E))[:4096]
+    edge = torch.tensor([0, 1, (1 << 26) - 1, 1 << 26, (1 << 26) + 1, T - 2, T - 1])
+    rows = torch.cat([rows, edge]).to(dev)
+    oi, ow = oracle.router(s[rows].cpu().numpy(), b.cpu().numpy(), K, G, TG, True, 2.5)
+    assert np.array_equal(idx[rows].cpu().numpy(), oi)
+    assert_weights_close(w[rows].cpu().numpy(), ow)
+    assert int((idx < 0).sum()) == 0  # every token written
+    del s, idx, w
+    torch.cuda.empty_cache()
