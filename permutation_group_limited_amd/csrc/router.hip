@@ -9,7 +9,8 @@
 // used): a token is owned by LPT consecutive lanes of a wave64, each lane
 // holding EPL consecutive experts (E = LPT * EPL). For E >= 64 a token fills
 // a whole wave (E = 256: 4 experts, one 16-byte load per lane); for E < 64
-// several tokens share a wave. E that is not a power of two takes a general
+// several tokens share a wave, and so do two tokens of 32 lanes each in
+// large batches at E = 64 ... 256 (RouterWideLaunch). E that is not a power of two takes a general
 // form (router_any_e_kernel): one wave per token with EPL * 64 >= E, absent
 // experts never candidates, and the group stage below replaced by a scan of
 // each group's scores staged in LDS.
@@ -57,6 +58,32 @@ struct RouterLaunch {
   }
 };
 
+// Two tokens per wave for E = 64 ... 256 (32 lanes per token, 2 * EPL
+// experts per lane): the K selection rounds serve two tokens at once and
+// the histogram merge sees twice the slots per workgroup, so a token costs
+// fewer instructions, but each wave's chain is longer. Reached through
+// dispatch_router with the one-token mapping (EPL, 64); used for large
+// batches only, where throughput rather than one wave's latency decides.
+template <typename DS, typename DB, int EPL, int LPT, int FN>
+struct RouterWideLaunch {
+  static moe_status_t run(int32_t* idx, void* w, const void* s, const void* b, int64_t T,
+                          int32_t K, int32_t G, int32_t TG, int32_t norm, float scale,
+                          int32_t mode, RouterHist hist, hipStream_t stream) {
+    if constexpr (LPT != kWave || EPL > 4) {
+      return MOE_ERR_UNSUPPORTED;
+    } else {
+      constexpr int TPB = kWavesPerBlock * 2;  // tokens per block
+      const int64_t blocks = (T + TPB - 1) / TPB;
+      hipLaunchKernelGGL((router_kernel<DS, DB, 2 * EPL, kWave / 2, FN>), grid_1d(blocks, kBlock),
+                         dim3(kBlock), 0, stream, idx, static_cast<typename DS::storage*>(w),
+                         static_cast<const typename DS::storage*>(s),
+                         static_cast<const typename DB::storage*>(b), T, K, G, TG, norm, scale,
+                         mode, hist);
+      return check_launch();
+    }
+  }
+};
+
 // Any E up to 1024 (not a power of two): one wave per token, EPL experts
 // per lane with EPL * 64 >= E, group stage through LDS.
 template <typename DS, typename DB, int EPL, int FN>
@@ -98,9 +125,19 @@ moe_status_t launch_router(int32_t* idx, void* w, const void* s, const void* b,
                            moe_dtype_t sd, moe_dtype_t bd, int32_t fn, int64_t T, int32_t E,
                            int32_t K, int32_t G, int32_t TG, int32_t norm, float scale,
                            int32_t mode, RouterHist hist, hipStream_t stream) {
-  if ((E & (E - 1)) == 0)
+  if ((E & (E - 1)) == 0) {
+    // two tokens per wave where it pays (measured, 20 launches per HIP
+    // graph): E = 64 ... 256, groups of at least 2 * E / 64 experts (whole
+    // lanes), T >= 8192, or >= 4096 when the router also fills the
+    // index histogram
+    const bool wide = E >= kWave && E <= 256 && G <= 32 &&
+                      T >= (hist.counts != nullptr ? 4096 : 8192);
+    if (wide)
+      return dispatch_router<RouterWideLaunch>(sd, bd, fn, E, idx, w, s, b, T, K, G, TG, norm,
+                                               scale, mode, hist, stream);
     return dispatch_router<RouterLaunch>(sd, bd, fn, E, idx, w, s, b, T, K, G, TG, norm, scale,
                                          mode, hist, stream);
+  }
   int32_t padded = kWave;
   while (padded < E) padded <<= 1;
   return dispatch_router<RouterAnyELaunch>(sd, bd, fn, padded, idx, w, s, b, T, K, G, TG, norm,

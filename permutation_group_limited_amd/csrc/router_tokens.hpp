@@ -359,8 +359,13 @@ __device__ __forceinline__ void route_tokens(
           static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(iw & 0xFu), win));
       const uint32_t id = static_cast<uint32_t>(win * EPL) + elem;
       if (lane == k) my_id = id;
-    } else {
+    } else if constexpr (EPL == 1) {
       if (sub == k) my_id = static_cast<uint32_t>(win - tok_lane0);  // one expert per lane
+    } else {
+      // several tokens per wave with EPL experts per lane: each segment's
+      // winner differs, so its element comes over ds_bpermute
+      const uint32_t elem = static_cast<uint32_t>(__shfl(static_cast<int>(iw & 0xFu), win, kWave));
+      if (sub == k) my_id = static_cast<uint32_t>((win - tok_lane0) * EPL) + elem;
     }
     if (lane == win) {
 #pragma unroll
@@ -376,8 +381,7 @@ __device__ __forceinline__ void route_tokens(
   // register) instead of reading the row again.
   const bool slot = tok_ok && sub < K;
   if (my_id >= static_cast<uint32_t>(E)) my_id = 0;  // unreachable with finite scores
-  const int owner = (LPT == kWave) ? static_cast<int>(my_id / EPL)
-                                   : tok_lane0 + static_cast<int>(my_id);
+  const int owner = tok_lane0 + static_cast<int>(my_id / EPL);
   const int elem = static_cast<int>(my_id % EPL);
   float u = 0.0f;
 #pragma unroll

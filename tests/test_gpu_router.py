@@ -212,3 +212,59 @@ def test_more_than_2_32_work_items(E, G, TG, K):
     assert int((idx < 0).sum()) == 0  # every token written
     del s, idx, w
     torch.cuda.empty_cache()
+
+
+# Large batches at E = 64 ... 256 with at most 32 groups take the two-tokens-
+# per-wave form (T >= 8192, or >= 4096 when the histogram is filled too);
+# 64 groups keep one token per wave. Ragged T leaves the last wave half used.
+WIDE = [(8195, 64, 8, 4, 8), (8195, 64, 32, 8, 16), (8192, 128, 1, 1, 8),
+        (8195, 128, 16, 4, 8), (8195, 256, 8, 4, 8), (8195, 256, 32, 4, 12),
+        (9001, 256, 16, 5, 10), (8195, 256, 64, 8, 8)]
+
+
+@pytest.mark.parametrize("T,E,G,TG,K", WIDE)
+@pytest.mark.parametrize("levels", [0, 3])
+def test_two_tokens_per_wave(T, E, G, TG, K, levels):
+    log("router wide", T, E, G, TG, K, "levels", levels)
+    s = wl.random_scores(T, E, seed=T + E + K + levels, levels=levels)
+    b = wl.random_bias(E, seed=G + TG, std=0.02, levels=levels)
+    for mode in (oracle.GROUP_TOP2_SUM, oracle.GROUP_MAX):
+        for norm in (True, False):
+            gi, gw = gpu_router(s, b, K, G, TG, norm, 1.75, mode)
+            oi, ow = oracle.router(s.numpy(), b.numpy(), K, G, TG, norm, 1.75, mode)
+            assert np.array_equal(gi, oi)
+            assert_weights_close(gw, ow)
+
+
+@pytest.mark.parametrize("sd,bd", [("bf16", "bf16"), ("f16", "f32")])
+def test_two_tokens_per_wave_16bit(sd, bd):
+    T, E, G, TG, K = 8195, 256, 8, 4, 8
+    log("router wide dtypes", sd, bd)
+    s = wl.random_scores(T, E, seed=3, levels=4).to(DTYPES[sd])
+    b = wl.random_bias(E, seed=4, std=0.02, levels=4).to(DTYPES[bd])
+    gi, gw = gpu_router(s, b, K, G, TG, True, 2.5)
+    sn, scode = encode(s)
+    bn, bcode = encode(b)
+    oi, ow = oracle.router(sn, bn, K, G, TG, True, 2.5, scores_dtype=scode,
+                           bias_dtype=None if bd == "f32" else bcode)
+    assert np.array_equal(gi, oi)
+    assert_16bit_within_one_ulp(bf16_bits(gw), ow, "router weights")
+
+
+@pytest.mark.parametrize("fn", ["sigmoid", "softmax"])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_two_tokens_per_wave_logits(fn, dt):
+    T, E, G, TG, K = 8195, 128, 8, 4, 8
+    log("router wide logits", fn, dt)
+    g = torch.Generator().manual_seed(17)
+    x = (torch.randn(T, E, generator=g) * 3).to(DTYPES[dt])
+    b = torch.randn(E, generator=g) * 0.02
+    gfn, ofn = FNS[fn]
+    gi, gw = gpu_router_logits(x, b, gfn, K, G, TG, True, 1.5)
+    xn, xcode = encode(x)
+    oi, ow = oracle.router(xn, b.numpy(), K, G, TG, True, 1.5, scores_dtype=xcode, score_fn=ofn)
+    assert np.array_equal(gi, oi)
+    if dt == "f32":
+        assert_weights_close(gw, ow)
+    else:
+        assert_16bit_within_one_ulp(bf16_bits(gw), ow, "router weights")
