@@ -9,7 +9,6 @@ namespace moe {
 namespace {
 thread_local int g_last_hip_error = 0;
 
-bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 size_t dtype_bytes(moe_dtype_t d) { return d == MOE_DTYPE_F32 ? 4 : 2; }
 bool dtype_ok(moe_dtype_t d) {

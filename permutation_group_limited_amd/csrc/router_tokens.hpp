@@ -61,6 +61,15 @@ template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
   return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), CTRL, 0xF, 0xF, true));
 }
+// v_writelane_b32: `value` (wave-uniform) into lane `lane` of `v`, other
+// lanes unchanged.
+extern "C" __device__ int moe_amdgcn_writelane(int value, int lane, int v) __asm(
+    "llvm.amdgcn.writelane.i32");
+__device__ __forceinline__ uint32_t write_lane(uint32_t value, int lane, uint32_t v) {
+  return static_cast<uint32_t>(
+      moe_amdgcn_writelane(static_cast<int>(value), lane, static_cast<int>(v)));
+}
+
 constexpr int kXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kHalfMirror = 0x141;  // lane i <-> 7-i within each 8 lanes
@@ -351,23 +360,38 @@ __device__ __forceinline__ void route_tokens(
   uint32_t my_id = 0;
   for (int k = 0; k < K; ++k) {
     const uint32_t head = kv[0];
-    const uint64_t bal = __ballot(head == segment_max<LPT>(head)) & segmask;
-    const int win = __builtin_ctzll(static_cast<unsigned long long>(bal));
+    const uint64_t top = __ballot(head == segment_max<LPT>(head));
+    bool pop;
     if constexpr (LPT == kWave) {
-      // the winner and its element are wave-uniform; slot k lives in lane k
+      // the winner and its element are wave-uniform; slot k goes to lane k
+      const int win = __builtin_ctzll(static_cast<unsigned long long>(top));
       const uint32_t elem =
           static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(iw & 0xFu), win));
-      const uint32_t id = static_cast<uint32_t>(win * EPL) + elem;
-      if (lane == k) my_id = id;
-    } else if constexpr (EPL == 1) {
-      if (sub == k) my_id = static_cast<uint32_t>(win - tok_lane0);  // one expert per lane
+      my_id = write_lane(static_cast<uint32_t>(win * EPL) + elem, k, my_id);
+      pop = lane == win;
+    } else if constexpr (LPT == kWave / 2 && EPL > 1) {
+      // two tokens per wave: each half's winner is the lowest set bit of its
+      // half of the ballot (every half has one: its maximum is one of its
+      // heads), so both winners, their elements and the two slot ids are
+      // wave-uniform; slot k of the tokens goes to lanes k and 32 + k
+      const int w_lo = __builtin_ctz(static_cast<uint32_t>(top));
+      const int w_hi = 32 + __builtin_ctz(static_cast<uint32_t>(top >> 32));
+      const uint32_t e4 = iw & 0xFu;
+      const uint32_t id_lo = static_cast<uint32_t>(w_lo * EPL) +
+                             static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(e4), w_lo));
+      const uint32_t id_hi = static_cast<uint32_t>((w_hi - 32) * EPL) +
+                             static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(e4), w_hi));
+      my_id = write_lane(id_lo, k, my_id);
+      my_id = write_lane(id_hi, 32 + k, my_id);
+      pop = lane == w_lo || lane == w_hi;
     } else {
-      // several tokens per wave with EPL experts per lane: each segment's
-      // winner differs, so its element comes over ds_bpermute
-      const uint32_t elem = static_cast<uint32_t>(__shfl(static_cast<int>(iw & 0xFu), win, kWave));
-      if (sub == k) my_id = static_cast<uint32_t>((win - tok_lane0) * EPL) + elem;
+      // one expert per lane, several tokens per wave
+      static_assert(EPL == 1, "several tokens per wave need one expert per lane or two tokens");
+      const int win = __builtin_ctzll(static_cast<unsigned long long>(top & segmask));
+      if (sub == k) my_id = static_cast<uint32_t>(win - tok_lane0);
+      pop = lane == win;
     }
-    if (lane == win) {
+    if (pop) {
 #pragma unroll
       for (int i = 0; i + 1 < EPL; ++i) kv[i] = kv[i + 1];
       kv[EPL - 1] = 0u;
