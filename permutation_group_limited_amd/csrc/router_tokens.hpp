@@ -370,10 +370,11 @@ __device__ __forceinline__ void route_tokens(
       my_id = write_lane(static_cast<uint32_t>(win * EPL) + elem, k, my_id);
       pop = lane == win;
     } else if constexpr (LPT == kWave / 2 && EPL > 1) {
-      // two tokens per wave: each half's winner is the lowest set bit of its
-      // half of the ballot (every half has one: its maximum is one of its
-      // heads), so both winners, their elements and the two slot ids are
-      // wave-uniform; slot k of the tokens goes to lanes k and 32 + k
+      // two tokens per wave (K <= 32, checked by the host): each half's
+      // winner is the lowest set bit of its half of the ballot (every half
+      // has one: its maximum is one of its heads), so both winners, their
+      // elements and the two slot ids are wave-uniform; slot k of the
+      // tokens goes to lanes k and 32 + k
       const int w_lo = __builtin_ctz(static_cast<uint32_t>(top));
       const int w_hi = 32 + __builtin_ctz(static_cast<uint32_t>(top >> 32));
       const uint32_t e4 = iw & 0xFu;

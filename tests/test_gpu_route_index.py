@@ -170,6 +170,7 @@ def test_workload_shapes(name, T, from_logits):
                                         # wave from T = 4096 (E = 64 ... 256, G <= 32)
                                         (4096, 256, 8, 4, 8), (4101, 128, 32, 4, 8),
                                         (4099, 64, 8, 4, 8), (4099, 256, 64, 8, 8),
+                                        (4099, 256, 8, 4, 40),
                                         (5000, 1024, 16, 4, 8), (2500, 8, 1, 1, 8),
                                         (100, 160, 8, 3, 6), (4096, 160, 8, 3, 6),
                                         (777, 20, 4, 3, 6), (3000, 1000, 8, 4, 8)])

@@ -214,12 +214,14 @@ def test_more_than_2_32_work_items(E, G, TG, K):
     torch.cuda.empty_cache()
 
 
-# Large batches at E = 64 ... 256 with at most 32 groups take the two-tokens-
-# per-wave form (T >= 8192, or >= 4096 when the histogram is filled too);
-# 64 groups keep one token per wave. Ragged T leaves the last wave half used.
+# Large batches at E = 64 ... 256 with at most 32 groups and K <= 32 take the
+# two-tokens-per-wave form (T >= 8192, or >= 4096 when the histogram is
+# filled too); 64 groups or K > 32 keep one token per wave. Ragged T leaves
+# the last wave half used.
 WIDE = [(8195, 64, 8, 4, 8), (8195, 64, 32, 8, 16), (8192, 128, 1, 1, 8),
         (8195, 128, 16, 4, 8), (8195, 256, 8, 4, 8), (8195, 256, 32, 4, 12),
-        (9001, 256, 16, 5, 10), (8195, 256, 64, 8, 8)]
+        (9001, 256, 16, 5, 10), (8195, 256, 64, 8, 8), (8195, 256, 8, 4, 32),
+        (8195, 256, 8, 4, 33), (8195, 128, 4, 4, 64), (8195, 64, 2, 2, 48)]
 
 
 @pytest.mark.parametrize("T,E,G,TG,K", WIDE)
