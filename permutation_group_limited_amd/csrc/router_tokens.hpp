@@ -54,10 +54,6 @@ __device__ __forceinline__ void load_row(float (&dst)[EPL],
 // lane of the same row, so no lane is left without a source; the moves are
 // written so that the compiler can fold them into the consuming VALU op.
 template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
   return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), CTRL, 0xF, 0xF, true));
 }
@@ -75,35 +71,40 @@ constexpr int kXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kHalfMirror = 0x141;  // lane i <-> 7-i within each 8 lanes
 constexpr int kMirror = 0x140;      // lane i <-> 15-i within each row
 
-// Merge the (largest, second largest) pair of this lane with the pair of
-// the lane that holds a disjoint set of experts.
-__device__ __forceinline__ void merge_top2(float& m1, float& m2, float o1, float o2) {
-  const float n2 = fmaxf(fminf(m1, o1), fmaxf(m2, o2));
-  m1 = fmaxf(m1, o1);
-  m2 = n2;
-}
-
-// Top-2 over groups of `lpg` adjacent lanes (lpg a power of two, groups
-// aligned). Each step pairs lanes whose partial results cover disjoint
-// experts: xor 1 and xor 2 (quad_perm), then the mirrored half-row and row
-// (every lane of a quad, resp. half-row, already holds the same pair), then
-// xor 16 (ds_swizzle) and xor 32 (ds_bpermute).
-__device__ __forceinline__ void group_top2(float& m1, float& m2, int lpg) {
-  if (lpg >= 2) merge_top2(m1, m2, dpp_f<kXor1>(m1), dpp_f<kXor1>(m2));
-  if (lpg >= 4) merge_top2(m1, m2, dpp_f<kXor2>(m1), dpp_f<kXor2>(m2));
-  if (lpg >= 8) merge_top2(m1, m2, dpp_f<kHalfMirror>(m1), dpp_f<kHalfMirror>(m2));
-  if (lpg >= 16) merge_top2(m1, m2, dpp_f<kMirror>(m1), dpp_f<kMirror>(m2));
-  if (lpg >= 32) {
-    const float o1 = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(m1), 0x401F));
-    const float o2 = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(m2), 0x401F));
-    merge_top2(m1, m2, o1, o2);
-  }
-  if (lpg >= 64) merge_top2(m1, m2, __shfl_xor(m1, 32, kWave), __shfl_xor(m2, 32, kWave));
-}
-
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t umin(uint32_t a, uint32_t b) { return a < b ? a : b; }
 
-// Sum over groups of `lpg` adjacent lanes, same lane pairing as group_top2.
+// Merge the (largest, second largest) pair of order-preserving keys of this
+// lane with the pair of the lane that holds a disjoint set of experts.
+__device__ __forceinline__ void merge_top2_keys(uint32_t& m1, uint32_t& m2, uint32_t o1,
+                                                uint32_t o2) {
+  m2 = umax(umin(m1, o1), umax(m2, o2));
+  m1 = umax(m1, o1);
+}
+
+// Top-2 keys over groups of `lpg` adjacent lanes (lpg a power of two,
+// groups aligned). Each step pairs lanes whose partial results cover
+// disjoint experts: xor 1 and xor 2 (quad_perm), then the mirrored half-row
+// and row (every lane of a quad, resp. half-row, already holds the same
+// pair), then xor 16 (ds_swizzle) and xor 32 (ds_bpermute).
+__device__ __forceinline__ void group_top2_keys(uint32_t& m1, uint32_t& m2, int lpg) {
+  if (lpg >= 2) merge_top2_keys(m1, m2, dpp_u<kXor1>(m1), dpp_u<kXor1>(m2));
+  if (lpg >= 4) merge_top2_keys(m1, m2, dpp_u<kXor2>(m1), dpp_u<kXor2>(m2));
+  if (lpg >= 8) merge_top2_keys(m1, m2, dpp_u<kHalfMirror>(m1), dpp_u<kHalfMirror>(m2));
+  if (lpg >= 16) merge_top2_keys(m1, m2, dpp_u<kMirror>(m1), dpp_u<kMirror>(m2));
+  if (lpg >= 32) {
+    const uint32_t o1 =
+        static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(m1), 0x401F));
+    const uint32_t o2 =
+        static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(m2), 0x401F));
+    merge_top2_keys(m1, m2, o1, o2);
+  }
+  if (lpg >= 64)
+    merge_top2_keys(m1, m2, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m1), 32, kWave)),
+                    static_cast<uint32_t>(__shfl_xor(static_cast<int>(m2), 32, kWave)));
+}
+
+// Sum over groups of `lpg` adjacent lanes, same lane pairing as group_top2_keys.
 __device__ __forceinline__ int group_sum(int x, int lpg) {
   if (lpg >= 2) x += __builtin_amdgcn_mov_dpp(x, kXor1, 0xF, 0xF, true);
   if (lpg >= 4) x += __builtin_amdgcn_mov_dpp(x, kXor2, 0xF, 0xF, true);
@@ -258,6 +259,10 @@ __device__ __forceinline__ void route_tokens(
   }
 #pragma unroll
   for (int i = 0; i < EPL; ++i) b[i] = s[i] + bi[i];
+  // order-preserving keys of the biased scores (group stage and top-K)
+  uint32_t bk[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) bk[i] = ordered_key(b[i]);
 
   // ---- group stage: keep the best topk_group groups ------------------------
   bool kept[EPL];
@@ -308,14 +313,19 @@ __device__ __forceinline__ void route_tokens(
     const int S = E >> lg_groups;
     const int LPG = S / EPL;  // lanes per group, a power of two
     const int lg_lpg = __builtin_ctz(static_cast<uint32_t>(LPG));
-    float m1 = -__builtin_inff(), m2 = -__builtin_inff();
+    // top-2 of the group on the order-preserving keys (exact integer max /
+    // min; key 0 lies below every finite score), then back to binary32 for
+    // the group score: the same values as the scores themselves (-0 reads
+    // back as +0, which compares equal)
+    uint32_t k1 = 0u, k2 = 0u;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-      m2 = fmaxf(m2, fminf(m1, b[i]));
-      m1 = fmaxf(m1, b[i]);
+      k2 = umax(umin(k1, k2), umin(umax(k1, k2), bk[i]));  // median of three: k1 >= k2
+      k1 = umax(k1, bk[i]);
     }
-    group_top2(m1, m2, LPG);
-    const float gs = (mode == MOE_GROUP_MAX || S == 1) ? m1 : m1 + m2;
+    group_top2_keys(k1, k2, LPG);
+    const float g1 = key_to_float(k1);
+    const float gs = (mode == MOE_GROUP_MAX || S == 1) ? g1 : g1 + key_to_float(k2);
     // rank of my group = groups that beat it; the LPG lanes of a group split
     // the comparisons (lane q of the group tests groups q, q + LPG, ...) and
     // add their counts
@@ -341,7 +351,7 @@ __device__ __forceinline__ void route_tokens(
   uint64_t pk[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
-    const uint32_t key = (tok_ok && kept[i] && present[i]) ? ordered_key(b[i]) : 0u;
+    const uint32_t key = (tok_ok && kept[i] && present[i]) ? bk[i] : 0u;
     pk[i] = (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(EPL - 1 - i);
   }
   sort_desc_u64<EPL>(pk);
