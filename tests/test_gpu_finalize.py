@@ -29,7 +29,8 @@ def _inputs(T, K, H, ddt, wdt, seed):
 @pytest.mark.parametrize("wdt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("odt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("T,K,H", [(1, 1, 8), (5, 2, 136), (33, 8, 520), (17, 3, 1032),
-                                   (9, 9, 264), (4, 16, 64), (40, 6, 7168), (3, 1, 4096)])
+                                   (9, 9, 264), (4, 16, 64), (40, 6, 7168), (3, 1, 4096),
+                                   (3, 64, 520)])
 def test_random_shapes(ddt, wdt, odt, T, K, H):
     if ddt == "f32" and H % 4 or ddt != "f32" and H % 8:
         pytest.skip("row not a multiple of 16 bytes")

@@ -158,6 +158,8 @@ def test_workload_shapes(name, T, from_logits):
                                         (32, 32, 8, 4, 6), (16, 64, 8, 3, 6), (16, 128, 8, 4, 8),
                                         (16, 256, 8, 4, 8), (9, 256, 8, 4, 8), (8, 512, 16, 4, 8),
                                         (4, 1024, 16, 4, 8), (3, 1024, 16, 4, 8),
+                                        (16, 256, 8, 8, 64), (4, 1024, 16, 16, 64),
+                                        (32, 32, 1, 1, 32),
                                         # two launches: one chunk or several, E a power of two
                                         # or not, just above the one-launch limits included
                                         (1025, 1, 1, 1, 1), (129, 8, 4, 2, 3), (33, 32, 8, 4, 6),
