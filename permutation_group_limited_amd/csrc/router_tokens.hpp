@@ -387,11 +387,11 @@ __device__ __forceinline__ void route_tokens(
       // tokens goes to lanes k and 32 + k
       const int w_lo = __builtin_ctz(static_cast<uint32_t>(top));
       const int w_hi = 32 + __builtin_ctz(static_cast<uint32_t>(top >> 32));
-      const uint32_t e4 = iw & 0xFu;
-      const uint32_t id_lo = static_cast<uint32_t>(w_lo * EPL) +
-                             static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(e4), w_lo));
-      const uint32_t id_hi = static_cast<uint32_t>((w_hi - 32) * EPL) +
-                             static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(e4), w_hi));
+      const int e4 = static_cast<int>(iw & 0xFu);
+      const uint32_t el_lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(e4, w_lo));
+      const uint32_t el_hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(e4, w_hi));
+      const uint32_t id_lo = static_cast<uint32_t>(w_lo * EPL) + el_lo;
+      const uint32_t id_hi = static_cast<uint32_t>((w_hi - 32) * EPL) + el_hi;
       my_id = write_lane(id_lo, k, my_id);
       my_id = write_lane(id_hi, 32 + k, my_id);
       pop = lane == w_lo || lane == w_hi;
