@@ -154,7 +154,7 @@ moe_status_t launch_router(int32_t* expert_indices, void* expert_weights, const 
                            RouterHist hist, hipStream_t stream);
 
 struct IndexPlan {
-  int waves;        // waves per workgroup (16 when E <= 256, else 4)
+  int waves;        // waves per workgroup (16 when E <= 256 and N > 512, else 4)
   int64_t chunk;    // slots per workgroup
   int64_t nchunks;  // workgroups of the scatter (and histogram) launch
   int rounds;       // 64-slot rounds per wave

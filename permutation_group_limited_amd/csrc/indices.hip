@@ -100,7 +100,10 @@ static int single_chunk_rounds(int32_t E, bool router_counts) {
 
 IndexPlan plan_indices(int64_t N, int32_t E, bool router_counts) {
   IndexPlan p;
-  p.waves = E <= 256 ? 16 : 4;  // W * E <= 4096 LDS words
+  // W * E <= 4096 LDS words; up to 512 slots 4 waves do it sooner (fewer
+  // threads in each barrier and scan: 4.4 against 5.0 us at N = 512,
+  // E = 256), above that 16 waves do
+  p.waves = (E <= 256 && N > 512) ? 16 : 4;
   const int64_t per_round = static_cast<int64_t>(p.waves) * kWave;
   if (N <= single_chunk_rounds(E, router_counts) * per_round) {
     // one workgroup does everything in one launch
