@@ -9,8 +9,8 @@ import oracle
 from permutation_group_limited_amd import binding
 from permutation_group_limited_amd import workloads as wl
 
-from _gpu import (DEV, assert_finalize_close, gpu_finalize, log, oracle_finalize_from,
-                  term_magnitude)
+from _gpu import (DEV, assert_finalize_close, bf16_bits, gpu_finalize, log,
+                  oracle_finalize_from, term_magnitude)
 
 pytestmark = pytest.mark.gpu
 
@@ -124,3 +124,26 @@ def test_more_than_2_32_work_items():
     assert_finalize_close(out[ts], exp, None)
     del down, out, restore
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("odt", ["f16", "bf16", "f32"])
+def test_overflow_to_infinity(odt):
+    """Sums past the output format's largest finite value round to +-inf
+    (round to nearest), equal bit for bit to the oracle: f16 past 65504,
+    bf16 and f32 past about 3.4e38 (fp32 accumulation overflows there)."""
+    T, K, H = 6, 2, 64
+    g = torch.Generator().manual_seed(9)
+    big = 3.0e38 if odt != "f16" else 4.0e4
+    down = torch.randn(T * K, H, generator=g)
+    down[:, :8] = big  # both terms large and of one sign: certain overflow
+    down[:, 8:16] = -big
+    w = torch.full((T, K), 1.5)
+    restore = np.arange(T * K, dtype=np.uint32)
+    got = gpu_finalize(down.to(DEV), restore, w, DT[odt])
+    exp = oracle_finalize_from(down, restore, w, DT[odt])
+    g_np = got.cpu()
+    assert torch.isinf(g_np[:, :16]).all()
+    if odt == "f32":
+        assert np.array_equal(g_np.numpy().view(np.uint32), np.asarray(exp).view(np.uint32))
+    else:
+        assert np.array_equal(bf16_bits(got), np.asarray(exp, np.uint16))
