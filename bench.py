@@ -246,6 +246,8 @@ def main():
                    "route_and_index": route_and_index, "finalize": finalize},
             replays=20 if wk.T * wk.K * wk.H > (1 << 31) else 100)
         result["extras"] = extras(wk, scores_h, bias_h, idx, wts, args.steps)
+        result["extras"]["two_batches_in_flight"] = two_batches_in_flight(
+            wk, scores, bias, down, args.steps)
 
     if args.copy_probe > 0:
         src = torch.ones(args.copy_probe // 4, dtype=torch.float32, device=dev)
@@ -417,6 +419,66 @@ def decode_latency(dk):
             "token_slots_per_s": T * K / (us * 1e-6),
             "token_slots_per_s_fused": T * K / (us_fused * 1e-6),
             "hbm_gbps": db / (us * 1e-6) / 1e9}
+
+
+def two_batches_in_flight(wk, scores, bias, down, steps):
+    """Throughput with two batches in flight, as micro-batch overlap in
+    serving runs them: the same step on two sets of output buffers on two
+    streams, alternating, so that one batch's routing and index creation
+    (latency-bound, few waves) runs beside the other batch's finalize
+    (HBM-bound). Every step is still the whole path on one batch; the
+    steps of one buffer set stay in order on its stream. Mean GPU time per
+    step over `steps` steps, and whether both sets end with the
+    single-stream output."""
+    import torch
+
+    from permutation_group_limited_amd import binding
+
+    dev = torch.device("cuda:0")
+    T, E, K, H = wk.T, wk.E, wk.K, wk.H
+    N = T * K
+
+    def buffers():
+        i32 = lambda *shape: torch.empty(shape, dtype=torch.int32, device=dev)  # noqa: E731
+        return {"idx": i32(T, K), "w": torch.empty(T, K, device=dev), "order": i32(N),
+                "restore": i32(N), "starts": i32(E + 1), "eids": i32(E), "stats": i32(2),
+                "ws": torch.zeros(binding.moe_route_and_index_workspace_size(T, K, E) // 4,
+                                  dtype=torch.int32, device=dev),
+                "out": torch.empty(T, H, dtype=wk.out_dtype, device=dev)}
+
+    sets = [buffers(), buffers()]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+
+    def step(b, st):
+        binding.moe_route_and_index(b["idx"], b["w"], b["order"], b["starts"], b["restore"],
+                                    b["eids"], b["stats"], scores, bias, b["ws"], wk.n_groups,
+                                    wk.topk_group, wk.norm_weights, wk.scale, stream=st)
+        binding.moe_finalize(b["out"], down, b["restore"], b["w"], stream=st)
+
+    def run(n, two):
+        cur = torch.cuda.current_stream()
+        a = torch.cuda.Event(enable_timing=True)
+        z = torch.cuda.Event(enable_timing=True)
+        a.record(cur)
+        for st in streams:
+            st.wait_event(a)
+        for k in range(n):
+            j = k % 2 if two else 0
+            step(sets[j], streams[j])
+        for st in streams:
+            cur.wait_stream(st)
+        z.record(cur)
+        torch.cuda.synchronize()
+        return a.elapsed_time(z) / n * 1e3
+
+    run(4, False)
+    single = run(steps, False)
+    ref = sets[0]["out"].clone()
+    run(4, True)
+    two = run(steps, True)
+    same = all(torch.equal(b["out"].view(torch.int16), ref.view(torch.int16)) for b in sets)
+    return {"us_per_step_one_stream": single, "us_per_step_two_streams": two,
+            "token_slots_per_s_two_streams": N / (two * 1e-6), "outputs_equal": bool(same)}
 
 
 def timing_protocol(step, stages, flush_bytes=1 << 30, replays=100):
