@@ -248,6 +248,8 @@ def main():
         result["extras"] = extras(wk, scores_h, bias_h, idx, wts, args.steps)
         result["extras"]["two_batches_in_flight"] = two_batches_in_flight(
             wk, scores, bias, down, args.steps)
+        result["extras"]["finalize_rotating_outputs"] = finalize_rotating_outputs(
+            wk, down, restore, wts, bytes_finalize, args.steps)
 
     if args.copy_probe > 0:
         src = torch.ones(args.copy_probe // 4, dtype=torch.float32, device=dev)
@@ -419,6 +421,34 @@ def decode_latency(dk):
             "token_slots_per_s": T * K / (us * 1e-6),
             "token_slots_per_s_fused": T * K / (us_fused * 1e-6),
             "hbm_gbps": db / (us * 1e-6) / 1e9}
+
+
+def finalize_rotating_outputs(wk, down, restore, wts, bytes_finalize, steps, n_out=8):
+    """finalize writing a different output buffer on each call (n_out of
+    them, used in turn), so that no output row is still held in the
+    memory-side cache from the call before, as it is when one output
+    buffer is rewritten back to back: mean time per call and the
+    algorithmic bandwidth, against 8 TB/s."""
+    import torch
+
+    from permutation_group_limited_amd import binding
+
+    outs = [torch.empty(wk.T, wk.H, dtype=wk.out_dtype, device="cuda:0") for _ in range(n_out)]
+    for o in outs:
+        binding.moe_finalize(o, down, restore, wts)
+    torch.cuda.synchronize()
+    n = max(n_out, (steps // n_out) * n_out)
+    a = torch.cuda.Event(enable_timing=True)
+    z = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for k in range(n):
+        binding.moe_finalize(outs[k % n_out], down, restore, wts)
+    z.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(z) / n * 1e3
+    gbps = bytes_finalize / (us * 1e-6) / 1e9
+    return {"buffers": n_out, "us_per_call": us, "achieved_gbps": gbps,
+            "frac": gbps / PEAK_HBM_GBPS}
 
 
 def two_batches_in_flight(wk, scores, bias, down, steps):
