@@ -134,7 +134,11 @@ __device__ __forceinline__ void scatter_chunk(
   int32_t first[kBatch];
   load_batch(first, ids, w0, 0, rounds, c1, lane);
   const bool split = nchunks > 1 && E <= kThreads;
-  const int parts = E <= kThreads ? kThreads / E : 1;
+  // no more parts than chunks: with few experts (E = 8: 128 parts of a
+  // 1024-thread block) the extra parts would only fold zeros, one LDS read
+  // after another, in step (b)
+  const int parts =
+      E <= kThreads ? static_cast<int>(nchunks < kThreads / E ? nchunks : kThreads / E) : 1;
   const int my_e = static_cast<int>(threadIdx.x) % E;
   const int my_part = static_cast<int>(threadIdx.x) / E;
   constexpr int kCountRegs = 16;
@@ -187,8 +191,9 @@ __device__ __forceinline__ void scatter_chunk(
   // (b) per-expert totals over all chunks and this chunk's prefix. Thread
   // tid owns experts [tid*EPT, tid*EPT + EPT), so a block scan over threads
   // followed by a local running sum is an exclusive scan over experts. When
-  // E <= threads, the column sums are split over P = threads / E parts
-  // (thread part*E + e reads chunks part, part + P, ...), so each thread has
+  // E <= threads, the column sums are split over P = min(threads / E,
+  // chunks) parts (thread part*E + e reads chunks part, part + P, ...), so
+  // each thread has
   // at most nchunks / P loads in flight, and are folded through LDS. The
   // W per-wave counts of an owned expert are read once, into registers.
   const int EPT = (E + kThreads - 1) / kThreads;
