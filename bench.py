@@ -654,37 +654,22 @@ def cpu_leg(wk, scores_h, bias_h, down, idx, wts, order, restore, starts, eids, 
     gw = wts.cpu().numpy()
     parity = {
         "router_indices": bool(np.array_equal(gi, oi)),
-        "router_weights": bool(np.all(np.abs(gw.astype(np.float64) - ow) <=
-                                      1e-6 * np.abs(ow.astype(np.float64)))),
+        "router_weights": bool(np.array_equal(gw.view(np.uint32), ow.view(np.uint32))),
         "create_indices": bool(np.array_equal(u32(order), ind["token_expert_order"]) and
                                np.array_equal(u32(restore), ind["restore_token_order"]) and
                                np.array_equal(u32(starts), ind["expert_start_indices"]) and
                                np.array_equal(eids.cpu().numpy(), ind["expert_ids"]) and
                                np.array_equal(u32(stats), ind["expert_usage_stats"])),
     }
-    # finalize ran on the GPU's own weights (within 1e-6 of the oracle's):
-    # accept 1 bf16 ulp, or (1e-6 + 2*K*2^-24) * sum|w*d| plus one spacing
+    # finalize ran on the GPU's own weights, equal to the oracle's bit for
+    # bit: every output within 1 bf16 ulp
     if ocode == oracle.BF16:
         gb = out.cpu().view(torch.int16).numpy().view(np.uint16)
-        g = oracle.bf16_to_f32(gb).astype(np.float64)
-        e = oracle.bf16_to_f32(o).astype(np.float64)
         ordg = np.where(gb & 0x8000, -(gb.astype(np.int64) & 0x7FFF), gb & 0x7FFF)
         orde = np.where(o & 0x8000, -(o.astype(np.int64) & 0x7FFF), o & 0x7FFF)
         ulp = np.abs(ordg - orde)
-        parity["finalize_max_ulp"] = int(ulp.max())
-        bad = ulp > 1
-        if bad.any():
-            rows_bad = np.unique(np.nonzero(bad)[0])
-            rsel = ind["restore_token_order"].reshape(T, K)[rows_bad].astype(np.int64)
-            dd = oracle.bf16_to_f32(d[rsel.reshape(-1)]).astype(np.float64).reshape(
-                rows_bad.size, K, -1)
-            mag = (np.abs(ow[rows_bad].astype(np.float64))[:, :, None] * np.abs(dd)).sum(1)
-            top = np.maximum(np.abs(g[rows_bad]), np.abs(e[rows_bad]))
-            spacing = np.exp2(np.floor(np.log2(np.where(top > 0, top, 1.0))) - 7.0)
-            within = np.abs(g[rows_bad] - e[rows_bad]) <= \
-                (1e-6 + 2 * K * 2.0 ** -24) * mag + spacing
-            bad[rows_bad] &= ~within
-        parity["finalize"] = not bool(bad.any())
+        parity["finalize_max_ulp"] = int(ulp.max(initial=0))
+        parity["finalize"] = bool(ulp.max(initial=0) <= 1)
     else:
         parity["finalize"] = bool(np.allclose(out.cpu().numpy(), o, rtol=1e-5, atol=1e-6))
     return baseline, parity

@@ -55,8 +55,9 @@ typedef enum {
     MOE_DTYPE_BF16 = 1, /* bfloat16 (high half of binary32) */
     MOE_DTYPE_F16 = 2   /* IEEE binary16 */
 } moe_dtype_t;
-/* Every value is widened exactly to binary32 on load; every result is
- * computed in binary32 and rounded to nearest even on store. */
+/* Every value is widened exactly to binary32 on load; results are
+ * computed in binary32 (router weights and score functions in binary64)
+ * and rounded to nearest even on store. */
 
 /* How a group of experts is scored before the top-topk_group groups are
  * kept. The router page keeps the best-scoring groups without saying how a
@@ -90,7 +91,9 @@ typedef enum {
  * Per token: b[e] = score[e] + bias[e] (fp32); groups ranked by group score
  * (ties: lower group index first), the first topk_group kept; among their
  * experts the K best by (b descending, expert index ascending) fill slots
- * 0..K-1 in that order; weight_k = score[e_k] (/ sum) * scale in fp32.
+ * 0..K-1 in that order; weight_k = score[e_k] (/ sum) * scale, evaluated in
+ * binary64 (sum over k = 0..K-1 in slot order, correctly rounded divide and
+ * product) and rounded once to binary32, then to the weights' dtype.
  *
  * Validation: T >= 0; E >= 1 and E % n_groups == 0; 1 <= topk_group <=
  * n_groups <= 64; 1 <= K <= topk_group * S; K <= 64; non-NULL pointers when
@@ -139,7 +142,9 @@ moe_status_t moe_router_group_limited_logits(int32_t* expert_indices, void* expe
 /*
  * moe_create_indices_workspace_size
  * Bytes of device workspace moe_create_indices needs for N slots and E
- * experts (0 when none is needed). Pure host computation; never fails.
+ * experts (0 when none is needed, and for E outside 1..1024). The size
+ * never decreases as N grows, so a buffer sized for the largest N serves
+ * every smaller one. Pure host computation; never fails.
  */
 size_t moe_create_indices_workspace_size(int64_t N, int32_t E);
 
@@ -211,9 +216,10 @@ moe_status_t moe_create_indices_aligned(uint32_t* token_expert_order,
 /*
  * moe_route_and_index_workspace_size
  * Bytes of device workspace moe_route_and_index needs for T tokens, K slots
- * per token and E experts: a counter word (256 bytes with padding) plus,
- * when the index step splits the T * K slots into several chunks, its
- * [chunks, E] uint32 counts matrix. 0 for arguments out of range. Pure host
+ * per token and E experts: a 256-byte header (a counter word and the status
+ * word) plus, when the index step may split the T * K slots into several
+ * chunks, room for its [chunks, E] uint32 counts matrix (at most 64 chunks).
+ * Never decreases as T grows. 0 for arguments out of range. Pure host
  * computation.
  */
 size_t moe_route_and_index_workspace_size(int64_t T, int32_t K, int32_t E);
@@ -249,16 +255,32 @@ size_t moe_route_and_index_workspace_size(int64_t T, int32_t K, int32_t E);
  *   workspace        device buffer of at least
  *                    moe_route_and_index_workspace_size(T, K, E) bytes,
  *                    4-byte aligned, ZERO-FILLED before its first use; every
- *                    call leaves it zero again (a buffer sized for the
- *                    largest batch serves every smaller one). Calls that
- *                    share a workspace must not run concurrently (one
- *                    stream, or ordered streams). A workspace that is not
- *                    zero gives wrong index outputs but no access outside
- *                    any buffer.
+ *                    call that returns MOE_OK leaves it zero again, except
+ *                    the status word below (a buffer sized for the largest
+ *                    batch serves every smaller one: the size never
+ *                    decreases as T grows). Calls that share a workspace
+ *                    must not run concurrently (one stream, or ordered
+ *                    streams). After a call that returned MOE_ERR_HIP the
+ *                    workspace must be zero-filled again before the next
+ *                    call (the router may have counted into it).
+ *
+ * Status word. The uint32 at byte offset MOE_ROUTE_INDEX_STATUS_OFFSET of
+ * the workspace is never cleared by the library. When the index step finds
+ * that the counts it was handed do not add up to T * K (the workspace was
+ * not zero on entry, or an expert id was out of range) it stores
+ * MOE_STATUS_COUNTS_MISMATCH there; the index outputs of that call are then
+ * unspecified (but written in bounds) and the counts are still cleared, so
+ * the next call starts clean. The caller may read the word (e.g. copy it to
+ * the host after the stream has finished) and reset it to 0. Only the
+ * two-launch form with several index chunks (T * K above one workgroup's
+ * share) takes counts from the router, so only it can report this.
  *
  * Validation: that of the two separate calls, and the workspace size. With T = 0 only the index
  * metadata outputs are written, as moe_create_indices does for N = 0.
  */
+#define MOE_ROUTE_INDEX_STATUS_OFFSET 4
+#define MOE_STATUS_COUNTS_MISMATCH 1u
+
 moe_status_t moe_route_and_index(int32_t* expert_indices, void* expert_weights,
                                  uint32_t* token_expert_order, uint32_t* expert_start_indices,
                                  uint32_t* restore_token_order, int32_t* expert_ids,

@@ -30,6 +30,11 @@ SCORE_NONE = 0
 SCORE_SIGMOID = 1
 SCORE_SOFTMAX = 2
 
+# moe_route_and_index workspace: byte offset of the status word, and the
+# value the index step stores there when the router's counts do not add up
+ROUTE_INDEX_STATUS_OFFSET = 4
+STATUS_COUNTS_MISMATCH = 1
+
 _STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
            3: "MOE_ERR_ALIGNMENT", 4: "MOE_ERR_WORKSPACE", 5: "MOE_ERR_HIP"}
 

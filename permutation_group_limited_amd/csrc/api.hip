@@ -102,9 +102,15 @@ moe_status_t moe_router_group_limited_logits(int32_t* expert_indices, void* expe
                        norm_weights, routed_scaling_factor, group_score, stream);
 }
 
+// A plan of several chunks never has more than kMaxChunks of them, so this
+// bound serves every N' <= N: the size never decreases as N grows.
+static size_t counts_bound(int32_t E) {
+  return static_cast<size_t>(kMaxChunks) * static_cast<size_t>(E) * sizeof(uint32_t);
+}
+
 size_t moe_create_indices_workspace_size(int64_t N, int32_t E) {
-  if (N < 0 || E < 1) return 0;
-  return plan_indices(N, E).workspace_bytes;
+  if (N < 0 || E < 1 || E > 1024) return 0;
+  return plan_indices(N, E).nchunks > 1 ? counts_bound(E) : 0;
 }
 
 // Index-output checks shared by the index entry points and the fused one
@@ -173,14 +179,15 @@ moe_status_t moe_create_indices_aligned(uint32_t* token_expert_order,
                         workspace_bytes, scales_offset, scale_align, stream);
 }
 
-// Workspace of moe_route_and_index: a counter word (padded to 256 bytes),
-// then, when the index step has several chunks, its counts matrix. Both are
-// zero between calls.
+// Workspace of moe_route_and_index: a 256-byte header (word 0 the ticket of
+// the scatter's workgroups, word 1 the status word), then, when the index
+// step may have several chunks, its counts matrix. Ticket and matrix are
+// zero between calls. Sized for the largest plan of any N' <= N.
 static constexpr size_t kTicketBytes = 256;
 
 static size_t route_index_workspace(int64_t N, int32_t E) {
   const IndexPlan plan = plan_indices(N, E, true);
-  return kTicketBytes + (plan.nchunks > 1 ? plan.workspace_bytes : 0);
+  return kTicketBytes + (plan.nchunks > 1 ? counts_bound(E) : 0);
 }
 
 size_t moe_route_and_index_workspace_size(int64_t T, int32_t K, int32_t E) {

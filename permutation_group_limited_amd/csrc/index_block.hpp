@@ -281,6 +281,14 @@ __device__ __forceinline__ void scatter_chunk(
   uint32_t excl[3], all[3], most;
   block_scan3<W>(mine, local_max, tmp, excl, all, &most);
   const uint32_t grand_total = all[0];
+  // Router-filled counts that do not add up to N mean the matrix was not
+  // zero on entry (or an id was out of range): report it in the status word
+  // of the workspace header. The outputs are then unspecified but in bounds,
+  // and the matrix is still cleared below.
+  if (ticket != nullptr && chunk_id == 0 && threadIdx.x == 0 &&
+      grand_total != static_cast<uint32_t>(N))
+    __hip_atomic_store(ticket + 1, static_cast<uint32_t>(MOE_STATUS_COUNTS_MISMATCH),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   uint32_t run = excl[0];
 #pragma unroll
   for (int j = 0; j < kMaxEPT; ++j) {

@@ -424,19 +424,22 @@ __device__ __forceinline__ void route_tokens(
     const float v = __shfl(s[i], owner, kWave);
     u = (i == elem) ? v : u;
   }
-  float w;
+  // Normalise and scale in binary64, rounded once to binary32: the sum of
+  // the K selected scores in slot order (each widened exactly), a correctly
+  // rounded divide, then the product with the scaling factor.
+  double wd = static_cast<double>(u);
   if (norm_weights) {
-    float d = 0.0f;
+    double d = 0.0;
     if constexpr (LPT == kWave) {
       for (int q = 0; q < K; ++q)
-        d += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, u), q));
+        d += static_cast<double>(
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, u), q)));
     } else {
-      for (int q = 0; q < K; ++q) d += __shfl(u, tok_lane0 + q, kWave);
+      for (int q = 0; q < K; ++q) d += static_cast<double>(__shfl(u, tok_lane0 + q, kWave));
     }
-    w = (u / d) * scale;
-  } else {
-    w = u * scale;
+    wd = wd / d;
   }
+  const float w = static_cast<float>(wd * static_cast<double>(scale));
   if (slot) {
     out_idx[t * K + sub] = static_cast<int32_t>(my_id);
     out_w[t * K + sub] = to_storage<DS>(w);

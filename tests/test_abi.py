@@ -94,10 +94,39 @@ def test_workspace_size(lib):
     assert lib.moe_create_indices_workspace_size(-1, 256) == 0
     # one workgroup (no workspace) up to 5 rounds of 1024 slots; 8 rounds for
     # E <= 16 and for E > 256 (rounds of 256 slots)
+    # past that, room for the counts of up to 64 chunks, whatever N
     ws = lib.moe_create_indices_workspace_size
-    assert ws(5120, 256) == 0 and ws(5121, 256) == 256 * 4 * 6
-    assert ws(8192, 8) == 0 and ws(8193, 8) == 8 * 4 * 9
-    assert ws(2048, 512) == 0 and ws(2049, 512) == 512 * 4 * 9
+    assert ws(5120, 256) == 0 and ws(5121, 256) == 256 * 4 * 64
+    assert ws(8192, 8) == 0 and ws(8193, 8) == 8 * 4 * 64
+    assert ws(2048, 512) == 0 and ws(2049, 512) == 512 * 4 * 64
+    assert ws(1 << 31, 1024) == 1024 * 4 * 64
+
+
+@pytest.mark.parametrize("E", [1, 8, 160, 256, 512, 1024])
+def test_workspace_sizes_never_decrease(lib, E):
+    """A workspace sized for the largest batch must serve every smaller one:
+    both size functions are non-decreasing in the problem size, checked over
+    every N up to 20,000 slots and around every chunk-count change of the
+    index plan (N = c * 64 * rounds-of-slots boundaries) up to 2^31."""
+    ci = lib.moe_create_indices_workspace_size
+    ri = lib.moe_route_and_index_workspace_size
+    ns = list(range(0, 20001))
+    for per_round in (256, 1024):
+        for r in range(1, 1 << 15, 97):
+            b = 64 * per_round * r
+            ns += [b - 1, b, b + 1, b + per_round * r + 1]
+    ns = sorted(set(n for n in ns if 0 <= n < (1 << 31)))
+    prev_c = prev_r = 0
+    for n in ns:
+        c = ci(n, E)
+        assert c >= prev_c, (n, c, prev_c)
+        prev_c = c
+    for n in ns:
+        if n % 8:
+            continue
+        r = ri(n // 8, 8, E)
+        assert r >= prev_r, (n, r, prev_r)
+        prev_r = r
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -181,10 +210,13 @@ def test_route_and_index_workspace_size(lib):
     assert ws(8192, 8, 256) == 256 + lib.moe_create_indices_workspace_size(65536, 256)
     assert ws(8192, 8, 256) > 256
     assert ws(100, 6, 160) == 256
-    # after the router has counted: one workgroup up to 4 rounds of 1024 slots
-    assert ws(512, 8, 256) == 256 and ws(513, 8, 256) == 256 + 256 * 4 * 5
-    assert ws(2048, 2, 8) == 256 and ws(2049, 2, 8) == 256 + 8 * 4 * 5
-    assert ws(256, 8, 512) == 256 and ws(257, 8, 512) == 256 + 512 * 4 * 9
+    # after the router has counted: one workgroup up to 4 rounds of 1024
+    # slots, past that room for the counts of up to 64 chunks
+    assert ws(512, 8, 256) == 256 and ws(513, 8, 256) == 256 + 256 * 4 * 64
+    assert ws(2048, 2, 8) == 256 and ws(2049, 2, 8) == 256 + 8 * 4 * 64
+    assert ws(256, 8, 512) == 256 and ws(257, 8, 512) == 256 + 512 * 4 * 64
+    # the case that once shrank: 8200 tokens needed less than 8192
+    assert ws(8200, 8, 256) >= ws(8192, 8, 256)
     assert ws(-1, 8, 256) == 0 and ws(8, 0, 256) == 0 and ws(8, 8, 2048) == 0
 
 

@@ -9,8 +9,8 @@ import oracle
 from permutation_group_limited_amd import binding
 from permutation_group_limited_amd import workloads as wl
 
-from _gpu import (DEV, assert_finalize_close, bf16_bits, gpu_finalize, log,
-                  oracle_finalize_from, term_magnitude)
+from _gpu import (DEV, assert_finalize_close, assert_finalize_matches_in_blocks, bf16_bits,
+                  gpu_finalize, log, oracle_finalize_from, term_magnitude)
 
 pytestmark = pytest.mark.gpu
 
@@ -68,24 +68,23 @@ def test_workload_full_size(name):
     assert_finalize_close(got, exp, mag)
 
 
-def test_skewed_full_size_sampled_tokens():
-    # full-size launch (7 GiB of down); the oracle checks 2048 sampled tokens,
-    # each of which depends only on its own K rows
+def test_skewed_full_size():
+    # full-size launch (7 GiB of down); every one of the 65,536 output rows
+    # is compared with the oracle, 4,096 tokens (470 MB of gathered rows) at
+    # a time
     wk = wl.WORKLOADS["skewed"]
-    log("finalize workload", wk.describe(), "(sampled)")
+    log("finalize workload", wk.describe(), "(all tokens, in blocks)")
     s, b = wl.make_scores(wk), wl.make_bias(wk)
-    ids, wts = oracle.router(s.numpy(), b.numpy(), 8, 8, 4, True, 2.5)
-    restore = oracle.create_indices(ids, 256)["restore_token_order"]
+    ids, wts = oracle.router(s.numpy(), b.numpy(), wk.K, wk.n_groups, wk.topk_group,
+                             wk.norm_weights, wk.scale)
+    restore = oracle.create_indices(ids, wk.E)["restore_token_order"]
     down = wl.make_down(wk, device=DEV)
-    got = gpu_finalize(down, restore, torch.from_numpy(wts), torch.bfloat16)
-    rng = np.random.default_rng(0)
-    ts = np.sort(np.concatenate([[0, wk.T - 1], rng.choice(wk.T, 2046, replace=False)]))
-    rows = restore.reshape(wk.T, 8)[ts].reshape(-1).astype(np.int64)
-    sub_down = down[torch.from_numpy(rows).to(DEV)].cpu()
-    sub_w = torch.from_numpy(wts[ts])
-    exp = oracle_finalize_from(sub_down, np.arange(rows.size, dtype=np.uint32), sub_w,
-                               torch.bfloat16)
-    assert_finalize_close(got[torch.from_numpy(ts).to(DEV)], exp, None)
+    got = gpu_finalize(down, restore, torch.from_numpy(wts), wk.out_dtype)
+    worst = assert_finalize_matches_in_blocks(got, down, restore, torch.from_numpy(wts),
+                                              wk.out_dtype)
+    log("skewed finalize: largest difference %s ulp" % worst)
+    del down, got
+    torch.cuda.empty_cache()
 
 
 def test_deterministic():

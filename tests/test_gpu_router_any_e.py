@@ -1,8 +1,8 @@
 """GPU parity of the router for expert counts that are not powers of two
 (any E up to 1024 with E % n_groups == 0; the router page leaves E to the
 caller). These take the kernel's general form: one wave per token, group
-stage through LDS. Indices bit-exact against the oracle; weights within
-1e-6 relative (fp32) or 1 ulp (16-bit). Marked gpu."""
+stage through LDS. Indices and weights (fp32 and 16-bit) bit-exact against the
+oracle. Marked gpu."""
 import numpy as np
 import pytest
 import torch
@@ -11,7 +11,7 @@ import oracle
 from permutation_group_limited_amd import binding
 from permutation_group_limited_amd import workloads as wl
 
-from _gpu import (DEV, assert_16bit_within_one_ulp, assert_indices_equal, assert_weights_close,
+from _gpu import (DEV, assert_indices_equal, assert_weights_equal,
                   bf16_bits, encode, gpu_indices, log)
 
 pytestmark = pytest.mark.gpu
@@ -47,9 +47,9 @@ def check(gi, gw, x, b, K, G, TG, norm, scale, mode=0, ofn=oracle.SCORE_LOAD):
                            bias_dtype=None if b.dtype == torch.float32 else bcode, score_fn=ofn)
     assert np.array_equal(gi, oi), "indices differ in %d tokens" % np.sum(np.any(gi != oi, 1))
     if x.dtype == torch.float32:
-        assert_weights_close(gw, ow)
+        assert_weights_equal(gw, ow)
     else:
-        assert_16bit_within_one_ulp(bf16_bits(gw), ow, "router weights")
+        assert_weights_equal(bf16_bits(gw), ow)
     return oi
 
 
