@@ -214,6 +214,37 @@ moe_status_t moe_create_indices_aligned(uint32_t* token_expert_order,
                                         uint32_t scale_align, void* stream);
 
 /*
+ * moe_create_indices_no_alloc
+ * For callers that cannot allocate device memory or pass a workspace (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): moe_create_indices with its counts matrix in a device array
+ * the library owns instead of a caller workspace. The call itself allocates
+ * nothing (no hipMalloc / hipFree or allocating library routine); the array
+ * is moe_create_indices_no_alloc_max_scratch_bytes() = 256 KiB (64 chunks x
+ * 1024 experts of uint32), held on each GPU the library runs on until the
+ * process ends. Its address is looked up once per device, on the first call
+ * made with that device current.
+ *
+ * Arguments, outputs, validation and determinism as moe_create_indices,
+ * without workspace and scales_offset_p. Every valid (N, E) fits the array;
+ * a plan that would not returns MOE_ERR_WORKSPACE. MOE_ERR_HIP if the
+ * array's address cannot be obtained.
+ *
+ * All calls on one GPU share that GPU's array, which keeps the last call's
+ * contents (nothing in it needs to be zero on entry). Calls that may overlap
+ * on one GPU (different streams without ordering, several host threads)
+ * race on it and give wrong outputs: serialise them.
+ */
+moe_status_t moe_create_indices_no_alloc(uint32_t* token_expert_order,
+                                         uint32_t* expert_start_indices,
+                                         uint32_t* restore_token_order, int32_t* expert_ids,
+                                         uint32_t* expert_usage_stats, const int32_t* topk_ids,
+                                         int64_t N, int32_t E, void* stream);
+
+/* Size in bytes of the device array moe_create_indices_no_alloc uses. */
+size_t moe_create_indices_no_alloc_max_scratch_bytes(void);
+
+/*
  * moe_route_and_index_workspace_size
  * Bytes of device workspace moe_route_and_index needs for T tokens, K slots
  * per token and E experts: a 256-byte header (a counter word and the status

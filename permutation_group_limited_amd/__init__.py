@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     load_library,
     moe_create_indices,
     moe_create_indices_aligned,
+    moe_create_indices_no_alloc,
     moe_create_indices_workspace_size,
     moe_finalize,
     moe_route_and_index,

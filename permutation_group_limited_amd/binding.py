@@ -93,6 +93,10 @@ def load_library(check_runtime: bool = True):
     lib.moe_create_indices_aligned.argtypes = [p, p, p, p, p, p, i64, i32, p, ctypes.c_size_t, p,
                                                ctypes.c_uint32, p]
     lib.moe_create_indices_aligned.restype = ctypes.c_int
+    lib.moe_create_indices_no_alloc.argtypes = [p, p, p, p, p, p, i64, i32, p]
+    lib.moe_create_indices_no_alloc.restype = ctypes.c_int
+    lib.moe_create_indices_no_alloc_max_scratch_bytes.argtypes = []
+    lib.moe_create_indices_no_alloc_max_scratch_bytes.restype = ctypes.c_size_t
     lib.moe_route_and_index_workspace_size.argtypes = [i64, i32, i32]
     lib.moe_route_and_index_workspace_size.restype = ctypes.c_size_t
     lib.moe_route_and_index.argtypes = [p, p, p, p, p, p, p, p, ctypes.c_uint32, p, p, i32, i32,
@@ -238,6 +242,35 @@ def moe_create_indices(token_expert_order: torch.Tensor, expert_start_indices: t
         _ptr(expert_ids), _ptr(expert_usage_stats), _ptr(topk_ids), n, E, _ptr(workspace),
         ws_bytes, scales_offset_p, _stream(stream, topk_ids, expert_ids))
     _check("moe_create_indices", st)
+
+
+def moe_create_indices_no_alloc(token_expert_order: torch.Tensor,
+                                expert_start_indices: torch.Tensor,
+                                restore_token_order: torch.Tensor, expert_ids: torch.Tensor,
+                                expert_usage_stats: torch.Tensor, topk_ids: torch.Tensor,
+                                stream=None) -> None:
+    """moe_create_indices without a workspace: the counts matrix lives in the
+    library's own device array (for callers that cannot allocate). Calls
+    that may overlap on one GPU race on that array."""
+    lib = load_library()
+    _dev(token_expert_order, expert_start_indices, restore_token_order, expert_ids,
+         expert_usage_stats, topk_ids)
+    for t, name in ((token_expert_order, "token_expert_order"),
+                    (expert_start_indices, "expert_start_indices"),
+                    (restore_token_order, "restore_token_order"), (expert_ids, "expert_ids"),
+                    (expert_usage_stats, "expert_usage_stats"), (topk_ids, "topk_ids")):
+        _int32_like(t, name)
+    n = topk_ids.numel()
+    E = expert_ids.numel()
+    if token_expert_order.numel() != n or restore_token_order.numel() != n:
+        raise ValueError("token_expert_order and restore_token_order need N entries")
+    if expert_start_indices.numel() != E + 1 or expert_usage_stats.numel() != 2:
+        raise ValueError("expert_start_indices needs E+1 entries, expert_usage_stats 2")
+    st = lib.moe_create_indices_no_alloc(
+        _ptr(token_expert_order), _ptr(expert_start_indices), _ptr(restore_token_order),
+        _ptr(expert_ids), _ptr(expert_usage_stats), _ptr(topk_ids), n, E,
+        _stream(stream, topk_ids, expert_ids))
+    _check("moe_create_indices_no_alloc", st)
 
 
 def moe_create_indices_aligned(token_expert_order: torch.Tensor,

@@ -140,6 +140,23 @@ def test_indices_validation(lib, kw, code):
     assert indices(lib, **kw) == code
 
 
+def test_no_alloc_scratch_size(lib):
+    # 64 chunks x 1024 experts of uint32: the largest counts matrix any plan needs
+    assert lib.moe_create_indices_no_alloc_max_scratch_bytes() == 64 * 1024 * 4
+    ws = lib.moe_create_indices_workspace_size
+    assert ws((1 << 32) - 1, 1024) <= lib.moe_create_indices_no_alloc_max_scratch_bytes()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=-1), INVALID), (dict(N=1 << 32), INVALID), (dict(E=0), INVALID),
+    (dict(E=1025), INVALID), (dict(ptrs=(FAKE, None) + (FAKE,) * 4), INVALID),
+    (dict(ptrs=(FAKE_ODD,) + (FAKE,) * 5, N=100), ALIGNMENT),
+])
+def test_no_alloc_validation(lib, kw, code):
+    p = kw.get("ptrs", (FAKE,) * 6)
+    assert lib.moe_create_indices_no_alloc(*p, kw.get("N", 100), kw.get("E", 256), None) == code
+
+
 def finalize(lib, T=4, K=2, H=64, od=1, dd=1, wd=0, ptrs=None):
     p = ptrs or (FAKE,) * 4
     return lib.moe_finalize(p[0], od, p[1], dd, p[2], p[3], wd, T, K, H, None)
