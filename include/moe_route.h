@@ -30,6 +30,12 @@
  *
  * Sizes are int64_t; T*K (the number of routed slots, N) must be below 2^32
  * because all slot indices are uint32.
+ *
+ * Enumerations. Each enum below carries *_ENUM_MIN / *_ENUM_MAX markers that
+ * span the whole int32 range, so that any int32 a caller passes is a value
+ * of the enum type (also in C++) and an unknown one is rejected by
+ * validation (MOE_ERR_INVALID_ARG) rather than being undefined. The markers
+ * are never valid arguments.
  */
 #ifndef MOE_ROUTE_H
 #define MOE_ROUTE_H
@@ -47,13 +53,17 @@ typedef enum {
     MOE_ERR_UNSUPPORTED = 2, /* valid request this build has no kernel for */
     MOE_ERR_ALIGNMENT = 3,   /* pointer or row size not 16-byte aligned */
     MOE_ERR_WORKSPACE = 4,   /* workspace missing or too small */
-    MOE_ERR_HIP = 5          /* HIP runtime rejected a launch */
+    MOE_ERR_HIP = 5,         /* HIP runtime rejected a launch */
+    MOE_STATUS_ENUM_MIN = -0x7FFFFFFF - 1, /* range markers (see below), never returned */
+    MOE_STATUS_ENUM_MAX = 0x7FFFFFFF
 } moe_status_t;
 
 typedef enum {
     MOE_DTYPE_F32 = 0,  /* IEEE binary32 */
     MOE_DTYPE_BF16 = 1, /* bfloat16 (high half of binary32) */
-    MOE_DTYPE_F16 = 2   /* IEEE binary16 */
+    MOE_DTYPE_F16 = 2,  /* IEEE binary16 */
+    MOE_DTYPE_ENUM_MIN = -0x7FFFFFFF - 1, /* range markers, not dtypes */
+    MOE_DTYPE_ENUM_MAX = 0x7FFFFFFF
 } moe_dtype_t;
 /* Every value is widened exactly to binary32 on load; results are
  * computed in binary32 (router weights and score functions in binary64)
@@ -64,7 +74,9 @@ typedef enum {
  * group's score is formed; two readings are offered. */
 typedef enum {
     MOE_GROUP_TOP2_SUM = 0, /* sum of the two largest biased scores in the group (default) */
-    MOE_GROUP_MAX = 1       /* largest biased score in the group */
+    MOE_GROUP_MAX = 1,      /* largest biased score in the group */
+    MOE_GROUP_ENUM_MIN = -0x7FFFFFFF - 1, /* range markers, not modes */
+    MOE_GROUP_ENUM_MAX = 0x7FFFFFFF
 } moe_group_score_t;
 
 /*
@@ -114,7 +126,9 @@ moe_status_t moe_router_group_limited(int32_t* expert_indices, void* expert_weig
 typedef enum {
     MOE_SCORE_NONE = 0,    /* the input already holds the scores */
     MOE_SCORE_SIGMOID = 1, /* score = 1 / (1 + exp(-logit)) */
-    MOE_SCORE_SOFTMAX = 2  /* score = softmax of the token's E logits */
+    MOE_SCORE_SOFTMAX = 2, /* score = softmax of the token's E logits */
+    MOE_SCORE_ENUM_MIN = -0x7FFFFFFF - 1, /* range markers, not functions */
+    MOE_SCORE_ENUM_MAX = 0x7FFFFFFF
 } moe_score_fn_t;
 
 /*
@@ -142,7 +156,7 @@ moe_status_t moe_router_group_limited_logits(int32_t* expert_indices, void* expe
 /*
  * moe_create_indices_workspace_size
  * Bytes of device workspace moe_create_indices needs for N slots and E
- * experts (0 when none is needed, and for E outside 1..1024). The size
+ * experts (0 when none is needed, and for N or E out of range). The size
  * never decreases as N grows, so a buffer sized for the largest N serves
  * every smaller one. Pure host computation; never fails.
  */

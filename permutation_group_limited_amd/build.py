@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmoe_route.so")
 SOURCES = ["api.hip", "router.hip", "indices.hip", "finalize.hip", "route_index.hip",
            "route_index_f32.hip", "route_index_bf16.hip", "route_index_f16.hip",
-           "no_alloc.hip"]
+           "no_alloc.hip", "plan.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -109,7 +109,7 @@ static size_t counts_bound(int32_t E) {
 }
 
 size_t moe_create_indices_workspace_size(int64_t N, int32_t E) {
-  if (N < 0 || E < 1 || E > 1024) return 0;
+  if (N < 0 || N > (int64_t)UINT32_MAX || E < 1 || E > 1024) return 0;
   return plan_indices(N, E).nchunks > 1 ? counts_bound(E) : 0;
 }
 
@@ -281,6 +281,7 @@ const char* moe_status_string(moe_status_t status) {
     case MOE_ERR_ALIGNMENT: return "misaligned pointer or row size";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_HIP: return "HIP runtime error";
+    default: break;
   }
   return "unknown status";
 }

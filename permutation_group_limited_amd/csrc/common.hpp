@@ -153,8 +153,10 @@ moe_status_t launch_router(int32_t* expert_indices, void* expert_weights, const 
                            int32_t topk_group, int32_t norm_weights, float scale, int32_t mode,
                            RouterHist hist, hipStream_t stream);
 
-// Index creation never splits a problem into more chunks than this.
+// Index creation never splits a problem into more chunks than this; its
+// waves load their ids kBatch rounds of 64 slots at a time.
 constexpr int64_t kMaxChunks = 64;
+constexpr int kBatch = 8;
 
 struct IndexPlan {
   int waves;        // waves per workgroup (16 when E <= 256 and N > 512, else 4)

@@ -9,7 +9,6 @@ namespace moe {
 namespace {
 
 constexpr int kMaxExperts = 1024;
-constexpr int kBatch = 8;  // 64-slot rounds loaded together per wave
 
 __device__ __forceinline__ int key_bits(int E) {
   int nb = 0;

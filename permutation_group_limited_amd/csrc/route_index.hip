@@ -1,5 +1,6 @@
 // Router and index creation in one launch (single-workgroup batches): dtype
-// dispatch and the batch limit. The kernel is in route_index_impl.hpp.
+// dispatch. The kernel is in route_index_impl.hpp, the batch limit in
+// plan.hip.
 #include "route_index.hpp"
 
 namespace moe {
@@ -24,14 +25,6 @@ moe_status_t launch_route_index(int32_t* idx, void* w, const void* s, const void
   if (sd == MOE_DTYPE_F16 && bd == MOE_DTYPE_F32) MOE_D(DF16, DF32);
 #undef MOE_D
   return MOE_ERR_UNSUPPORTED;
-}
-
-int64_t route_index_max_tokens(int32_t E) {
-  // W * (64 / LPT) with W = min(16, 4096 / E) waves and LPT = min(E, 64)
-  if (E < 1 || E > 1024 || (E & (E - 1)) != 0) return 0;
-  const int64_t waves = E <= 256 ? 16 : 4096 / E;
-  const int64_t lanes_per_token = E < kWave ? E : kWave;
-  return waves * (kWave / lanes_per_token);
 }
 
 }  // namespace moe
