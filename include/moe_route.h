@@ -280,10 +280,17 @@ size_t moe_route_and_index_workspace_size(int64_t T, int32_t K, int32_t E);
  *     (16 tokens for E in 64..256, 8 for 512, 4 for 1024, 64 * 16 / E
  *     below 64): one launch, that workgroup routing every token and then
  *     building the index outputs;
- *   - otherwise two launches: the router also counts each chunk's slots per
- *     expert (relaxed atomic adds into the workspace's counts matrix), so
- *     the index step needs no histogram pass of its own; its last
- *     workgroup clears the matrix again.
+ *   - otherwise two launches. For E <= 256, batches of at most 2048
+ *     router workgroups and a 16-byte aligned workspace (ranked form),
+ *     the router also ranks each slot
+ *     among the earlier slots of its workgroup with the same expert and
+ *     records each workgroup's count per expert (scratch in the workspace
+ *     and in restore_token_order), so that the index step places every
+ *     slot directly; above one index chunk it also adds the counts into
+ *     the workspace's counts matrix (relaxed atomic adds). Otherwise
+ *     (chunked form) the router counts each chunk's slots per expert into
+ *     that matrix, so the index step needs no histogram pass of its own.
+ *     In both, the index step's last workgroup clears the matrix again.
  *
  *   expert_indices, expert_weights       out as moe_router_group_limited.
  *   token_expert_order ... expert_usage_stats
@@ -299,10 +306,14 @@ size_t moe_route_and_index_workspace_size(int64_t T, int32_t K, int32_t E);
  *   expert_bias, scalars                 as moe_router_group_limited.
  *   workspace        device buffer of at least
  *                    moe_route_and_index_workspace_size(T, K, E) bytes,
- *                    4-byte aligned, ZERO-FILLED before its first use; every
- *                    call that returns MOE_OK leaves it zero again, except
- *                    the status word below (a buffer sized for the largest
- *                    batch serves every smaller one: the size never
+ *                    4-byte aligned, ZERO-FILLED before its first use. Its
+ *                    first 256 + 64 * E' * 4 bytes, E' = E rounded up to a
+ *                    multiple of 4 (or all of it, if it is
+ *                    smaller) hold a header and a counts matrix that every
+ *                    call returning MOE_OK leaves zero again, except the
+ *                    status word below; bytes past them are scratch that a
+ *                    call may leave holding anything. A buffer sized for the
+ *                    largest batch serves every smaller one (the size never
  *                    decreases as T grows). Calls that share a workspace
  *                    must not run concurrently (one stream, or ordered
  *                    streams). After a call that returned MOE_ERR_HIP the
@@ -311,14 +322,13 @@ size_t moe_route_and_index_workspace_size(int64_t T, int32_t K, int32_t E);
  *
  * Status word. The uint32 at byte offset MOE_ROUTE_INDEX_STATUS_OFFSET of
  * the workspace is never cleared by the library. When the index step finds
- * that the counts it was handed do not add up to T * K (the workspace was
- * not zero on entry, or an expert id was out of range) it stores
- * MOE_STATUS_COUNTS_MISMATCH there; the index outputs of that call are then
- * unspecified (but written in bounds) and the counts are still cleared, so
- * the next call starts clean. The caller may read the word (e.g. copy it to
- * the host after the stream has finished) and reset it to 0. Only the
- * two-launch form with several index chunks (T * K above one workgroup's
- * share) takes counts from the router, so only it can report this.
+ * that the counts matrix it was handed does not add up to T * K (the
+ * workspace was not zero on entry) it stores MOE_STATUS_COUNTS_MISMATCH
+ * there; the index outputs of that call are then unspecified (but written
+ * in bounds) and the matrix is still cleared, so the next call starts
+ * clean. The caller may read the word (e.g. copy it to the host after the
+ * stream has finished) and reset it to 0. Only calls whose index step has
+ * several chunks use the matrix, so only they can report this.
  *
  * Validation: that of the two separate calls, and the workspace size. With T = 0 only the index
  * metadata outputs are written, as moe_create_indices does for N = 0.

@@ -1,4 +1,5 @@
-"""Build ``libmoe_route.so`` (the gfx950 HIP library) in-tree with hipcc.
+"""Build ``libmoe_route.so`` (the gfx950 HIP library) and ``libmoe_probe.so``
+(bandwidth probes for the benchmark) in-tree with hipcc.
 
     python -m permutation_group_limited_amd.build
 
@@ -19,6 +20,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmoe_route.so")
+# bandwidth probes timed by the benchmark beside the routing path
+PROBE_LIB = os.path.join(HERE, "libmoe_probe.so")
+PROBE_SOURCES = ["probe.hip"]
 SOURCES = ["api.hip", "router.hip", "indices.hip", "finalize.hip", "route_index.hip",
            "route_index_f32.hip", "route_index_bf16.hip", "route_index_f16.hip",
            "no_alloc.hip", "plan.hip"]
@@ -43,29 +47,45 @@ def _run(cmd, verbose):
     return r.returncode, msgs
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source to an object (in parallel), then link."""
-    tmpdir = tempfile.mkdtemp(prefix="moe_build_")
-    try:
-        objs = [os.path.join(tmpdir, s.replace(".hip", ".o")) for s in SOURCES]
-        cmds = [[HIPCC] + FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, s),
-                                   "-o", o] for s, o in zip(SOURCES, objs)]
-        jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
-        with ThreadPoolExecutor(jobs) as ex:
-            results = list(ex.map(lambda c: _run(c, verbose), cmds))
-        for (rc, msgs), src in zip(results, SOURCES):
-            if rc != 0:
-                sys.stderr.write("\n".join(msgs) + "\n")
-                raise RuntimeError("hipcc failed compiling %s" % src)
-            if verbose and msgs:
-                sys.stderr.write("\n".join(msgs) + "\n")
-        tmp = LIB + ".tmp%d" % os.getpid()
-        rc, msgs = _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs +
-                        ["-o", tmp], verbose)
+def _compile_all(jobs_list, verbose):
+    jobs = max(1, min(len(jobs_list), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(lambda c: _run(c[0], verbose), jobs_list))
+    for (rc, msgs), (_, src) in zip(results, jobs_list):
         if rc != 0:
             sys.stderr.write("\n".join(msgs) + "\n")
-            raise RuntimeError("hipcc failed linking %s" % LIB)
-        os.replace(tmp, LIB)
+            raise RuntimeError("hipcc failed compiling %s" % src)
+        if verbose and msgs:
+            sys.stderr.write("\n".join(msgs) + "\n")
+
+
+def _link(objs, lib, verbose):
+    tmp = lib + ".tmp%d" % os.getpid()
+    rc, msgs = _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp],
+                    verbose)
+    if rc != 0:
+        sys.stderr.write("\n".join(msgs) + "\n")
+        raise RuntimeError("hipcc failed linking %s" % lib)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link the routing
+    library and the probe library."""
+    tmpdir = tempfile.mkdtemp(prefix="moe_build_")
+    try:
+        groups = [(LIB, SOURCES), (PROBE_LIB, PROBE_SOURCES)]
+        jobs, objs = [], {}
+        for lib, srcs in groups:
+            objs[lib] = []
+            for s in srcs:
+                o = os.path.join(tmpdir, s.replace(".hip", ".o"))
+                objs[lib].append(o)
+                jobs.append(([HIPCC] + FLAGS + ["-I", INCLUDE, "-I", CSRC, "-c",
+                                                os.path.join(CSRC, s), "-o", o], s))
+        _compile_all(jobs, verbose)
+        for lib, _ in groups:
+            _link(objs[lib], lib, verbose)
     finally:
         shutil.rmtree(tmpdir, ignore_errors=True)
     return LIB

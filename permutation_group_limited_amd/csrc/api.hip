@@ -180,19 +180,38 @@ moe_status_t moe_create_indices_aligned(uint32_t* token_expert_order,
 }
 
 // Workspace of moe_route_and_index: a 256-byte header (word 0 the ticket of
-// the scatter's workgroups, word 1 the status word), then, when the index
-// step may have several chunks, its counts matrix. Ticket and matrix are
-// zero between calls. Sized for the largest plan of any N' <= N.
+// the scatter's workgroups, word 1 the status word), then room for a counts
+// matrix of kMaxChunks rows (zero between calls, with the ticket; rows of E
+// words in the chunked form, of ranked_stride(E) in the ranked form), then,
+// for the ranked form, room for the router's fine rows of counts (scratch:
+// fully rewritten by every call that uses them). Sized for the largest plan of
+// any T' <= T, so the size never decreases as T grows.
 static constexpr size_t kTicketBytes = 256;
 
-static size_t route_index_workspace(int64_t N, int32_t E) {
-  const IndexPlan plan = plan_indices(N, E, true);
-  return kTicketBytes + (plan.nchunks > 1 ? counts_bound(E) : 0);
+static bool two_launch_possible(int64_t T, int32_t E) { return T > route_index_max_tokens(E); }
+
+static size_t ranked_counts_bytes(int32_t E) {
+  return static_cast<size_t>(kMaxChunks) * static_cast<size_t>(ranked_stride(E)) *
+         sizeof(uint32_t);
+}
+
+static size_t route_index_workspace(int64_t T, int32_t K, int32_t E) {
+  const bool ranked = E <= kRankedMaxExperts && two_launch_possible(T, E);
+  const bool chunked = plan_indices(T * K, E, true).nchunks > 1;
+  size_t bytes = kTicketBytes;
+  if (ranked)
+    bytes += ranked_counts_bytes(E);
+  else if (chunked)
+    bytes += counts_bound(E);
+  if (ranked)
+    bytes += static_cast<size_t>(ranked_fine_rows_bound(T)) *
+             static_cast<size_t>(ranked_stride(E)) * sizeof(uint32_t);
+  return bytes;
 }
 
 size_t moe_route_and_index_workspace_size(int64_t T, int32_t K, int32_t E) {
   if (T < 0 || K < 1 || E < 1 || E > 1024 || T > (int64_t)UINT32_MAX / K) return 0;
-  return route_index_workspace(T * K, E);
+  return route_index_workspace(T, K, E);
 }
 
 moe_status_t moe_route_and_index(int32_t* expert_indices, void* expert_weights,
@@ -218,7 +237,7 @@ moe_status_t moe_route_and_index(int32_t* expert_indices, void* expert_weights,
                            expert_ids, expert_usage_stats, expert_indices, N, E, scales_offset,
                            scale_align);
   if (st != MOE_OK) return st;
-  if (workspace == nullptr || workspace_bytes < route_index_workspace(N, E))
+  if (workspace == nullptr || workspace_bytes < route_index_workspace(T, K, E))
     return MOE_ERR_WORKSPACE;
   if (!aligned(workspace, 4)) return MOE_ERR_ALIGNMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -236,8 +255,27 @@ moe_status_t moe_route_and_index(int32_t* expert_indices, void* expert_weights,
                               static_cast<int32_t>(group_score), token_expert_order,
                               expert_start_indices, restore_token_order, expert_ids,
                               expert_usage_stats, scales_offset, scale_align, s);
-  // two launches: the router also fills the index step's counts matrix,
-  // then the scatter (which clears the matrix again) takes no histogram pass
+  const RankedPlan rp = plan_ranked(T, K, E, n_groups);
+  if (rp.ok && aligned(workspace, 16)) {  // its rows of counts move in 16-byte pieces
+    // two launches, ranked form: the router ranks every slot within its
+    // workgroup and records its row of counts (and adds it into the counts
+    // matrix when there are several chunks); the index step places each
+    // slot from those alone
+    uint32_t* fine = counts + ranked_counts_bytes(E) / sizeof(uint32_t);
+    uint32_t* coarse = rp.nchunks > 1 ? counts : nullptr;
+    const moe_status_t rs = launch_router(
+        expert_indices, expert_weights, router_input, expert_bias, input_dtype, bias_dtype,
+        static_cast<int32_t>(score_fn), T, E, K, n_groups, topk_group, norm_weights ? 1 : 0,
+        routed_scaling_factor, static_cast<int32_t>(group_score),
+        RouterHist{coarse, 0u, fine, restore_token_order, rp.R}, s);
+    if (rs != MOE_OK) return rs;
+    return launch_indices_ranked(token_expert_order, expert_start_indices, restore_token_order,
+                                 expert_ids, expert_usage_stats, scales_offset, scale_align, N, E,
+                                 fine, coarse, ticket, rp, s);
+  }
+  // two launches, chunked form: the router also fills the index step's
+  // counts matrix, then the scatter (which clears the matrix again) takes
+  // no histogram pass
   const bool multi = plan.nchunks > 1;
   const moe_status_t rs = launch_router(
       expert_indices, expert_weights, router_input, expert_bias, input_dtype, bias_dtype,

@@ -138,13 +138,56 @@ __device__ __forceinline__ uint64_t match_any(uint32_t key, int nbits, uint64_t 
 
 // ---- launchers (host side), one per stage --------------------------------
 
-// Per-chunk expert histogram that the router can fill for the index step:
-// counts is index creation's counts matrix [nchunks, E] (uint32, zero on
-// entry), chunk its slots per chunk. counts == NULL: no histogram.
+// Index creation never splits a problem into more chunks than this; its
+// waves load their ids kBatch rounds of 64 slots at a time.
+constexpr int64_t kMaxChunks = 64;
+constexpr int kBatch = 8;
+
+
+// What the router records for the index step (moe_route_and_index).
+// Chunked form (fine == NULL): counts is index creation's counts matrix
+// [nchunks, E] (uint32, zero on entry), chunk its slots per chunk;
+// counts == NULL and fine == NULL: no histogram.
+// Ranked form (fine != NULL): router workgroup b writes row b of `fine`
+// [router workgroups, ranked_stride(E)] (its slots per expert), stores for
+// each of its slots (rank << 10) | expert in `packed` (rank = earlier slots
+// of the workgroup with the same expert), and, when counts != NULL, adds
+// its counts into row b / rows_per_chunk of counts [chunks,
+// ranked_stride(E)] (zero on entry).
 struct RouterHist {
   uint32_t* counts;
   uint32_t chunk;
+  uint32_t* fine;
+  uint32_t* packed;
+  uint32_t rows_per_chunk;
 };
+constexpr uint32_t kPackedExpertBits = 10;
+
+// Tokens per router workgroup for a batch of T tokens (`counting`: the
+// router also records the index step's counts), and whether that launch
+// takes two tokens per wave. Shared by the router launcher and the index
+// planner so that both see the same workgroups.
+bool router_two_tokens_per_wave(int64_t T, int32_t E, int32_t K, int32_t G, bool counting);
+int32_t router_block_tokens(int64_t T, int32_t E, int32_t K, int32_t G, bool counting);
+
+// Ranked form of moe_route_and_index: fine rows of F slots (one per router
+// workgroup), R rows per index chunk, nchunks chunks (counts matrix only
+// when nchunks > 1). ok == false: the batch takes the chunked form.
+struct RankedPlan {
+  bool ok;
+  uint32_t F;
+  uint32_t rows;
+  uint32_t R;
+  int64_t nchunks;
+};
+constexpr uint32_t kRankedMaxRowsPerChunk = 32;
+// Rows of counts in the ranked form have a stride of E rounded up to a
+// multiple of 4 (padding entries zero), so that they move in 16-byte pieces.
+__host__ __device__ constexpr int32_t ranked_stride(int32_t E) { return (E + 3) & ~3; }
+constexpr int32_t kRankedMaxExperts = 256;
+RankedPlan plan_ranked(int64_t T, int32_t K, int32_t E, int32_t G);
+// Rows of fine counts a moe_route_and_index workspace holds room for.
+int64_t ranked_fine_rows_bound(int64_t T);
 
 // score_fn: 0 = scores given, 1 = sigmoid of logits, 2 = softmax of logits
 moe_status_t launch_router(int32_t* expert_indices, void* expert_weights, const void* scores,
@@ -153,10 +196,6 @@ moe_status_t launch_router(int32_t* expert_indices, void* expert_weights, const 
                            int32_t topk_group, int32_t norm_weights, float scale, int32_t mode,
                            RouterHist hist, hipStream_t stream);
 
-// Index creation never splits a problem into more chunks than this; its
-// waves load their ids kBatch rounds of 64 slots at a time.
-constexpr int64_t kMaxChunks = 64;
-constexpr int kBatch = 8;
 
 struct IndexPlan {
   int waves;        // waves per workgroup (16 when E <= 256 and N > 512, else 4)
@@ -180,6 +219,15 @@ moe_status_t launch_indices(uint32_t* token_expert_order, uint32_t* expert_start
                             uint32_t scale_align, const int32_t* topk_ids, int64_t N, int32_t E,
                             void* workspace, const IndexPlan& plan, bool counts_ready,
                             uint32_t* ticket, hipStream_t stream);
+
+// Index step of the ranked form: from the router's fine rows (and counts
+// matrix when plan.nchunks > 1) and packed slots, every index output.
+moe_status_t launch_indices_ranked(uint32_t* token_expert_order, uint32_t* expert_start_indices,
+                                   uint32_t* restore_token_order, int32_t* expert_ids,
+                                   uint32_t* expert_usage_stats, uint32_t* scales_offset,
+                                   uint32_t scale_align, int64_t N, int32_t E,
+                                   const uint32_t* fine, uint32_t* counts, uint32_t* ticket,
+                                   const RankedPlan& plan, hipStream_t stream);
 
 // Router and index creation in one launch, for batches that one workgroup
 // routes alone (T <= route_index_max_tokens(E)).

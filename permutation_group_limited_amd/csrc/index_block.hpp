@@ -44,12 +44,17 @@ __device__ __forceinline__ uint32_t wave_inclusive(uint32_t x) {
 // values v[] in thread order (excl[]), their block totals (all[]) and the
 // block maximum of m. `tmp` is 4 * W words of LDS, not touched again by the
 // caller before its next workgroup barrier. Must be reached by every thread.
+// Each wave scans in registers; lane 63 publishes the wave's totals; after
+// one barrier lanes 0..W-1 of every wave read the W totals of each value and
+// scan them (W <= 16: one row of lanes), and v_readlane gives the wave its
+// offset and the block total.
 template <int W>
 __device__ __forceinline__ void block_scan3(const uint32_t (&v)[3], uint32_t m, uint32_t* tmp,
                                             uint32_t (&excl)[3], uint32_t (&all)[3],
                                             uint32_t* most) {
+  static_assert(W <= 16, "the wave totals are scanned within one row of 16 lanes");
   const int lane = lane_id();
-  const int wave = static_cast<int>(threadIdx.x) / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
   uint32_t x[3];
 #pragma unroll
   for (int q = 0; q < 3; ++q) x[q] = wave_inclusive<false>(v[q]);
@@ -60,22 +65,17 @@ __device__ __forceinline__ void block_scan3(const uint32_t (&v)[3], uint32_t m, 
     tmp[3 * W + wave] = m;
   }
   __syncthreads();
-  uint32_t mx = 0;
 #pragma unroll
   for (int q = 0; q < 3; ++q) {
-    uint32_t before = 0, sum = 0;
-#pragma unroll
-    for (int w = 0; w < W; ++w) {
-      const uint32_t tw = tmp[q * W + w];
-      before += (w < wave) ? tw : 0u;
-      sum += tw;
-    }
+    const uint32_t s = wave_inclusive<false>(lane < W ? tmp[q * W + lane] : 0u);
+    const uint32_t before =
+        wave > 0 ? static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(s), wave - 1))
+                 : 0u;
     excl[q] = before + x[q] - v[q];
-    all[q] = sum;
+    all[q] = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(s), W - 1));
   }
-#pragma unroll
-  for (int w = 0; w < W; ++w) mx = mx > tmp[3 * W + w] ? mx : tmp[3 * W + w];
-  *most = mx;
+  const uint32_t mm = wave_inclusive<true>(lane < W ? tmp[3 * W + lane] : 0u);
+  *most = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mm), W - 1));
 }
 
 // Loads rounds [r0, r0 + kBatch) of this wave's sub-range: lane value, or -1
@@ -97,12 +97,13 @@ __device__ __forceinline__ void load_batch(int32_t (&ev)[kBatch], const int32_t*
 // thread of the workgroup.
 //
 // ticket != NULL (several chunks, counts filled by the router's atomics):
-// after its scatter, thread 0 adds one to *ticket; the workgroup that draws
-// the last ticket clears the matrix (nchunks * E words) and the ticket, so
-// that both are zero for the next call. Only a read-before-write order is
-// needed (every workgroup has consumed its loads of the matrix before its
-// add, and the clearing stores are issued after the last add returns), so
-// the add is relaxed: no cache write-back or invalidation per workgroup.
+// once the workgroup has consumed its loads of the matrix, thread 0 adds
+// one to *ticket; after its scatter, the workgroup that drew the last
+// ticket clears the matrix (nchunks * E words) and the ticket, so that both
+// are zero for the next call. Only a read-before-write order is needed
+// (every workgroup has consumed its loads of the matrix before its add, and
+// the clearing stores are issued after the last add returns), so the add is
+// relaxed: no cache write-back or invalidation per workgroup.
 template <int W>
 __device__ __forceinline__ void scatter_chunk(
     uint32_t* __restrict__ order, uint32_t* __restrict__ starts, uint32_t* __restrict__ restore,
@@ -279,6 +280,12 @@ __device__ __forceinline__ void scatter_chunk(
   const uint32_t mine[3] = {local_sum, local_active, local_pad};
   uint32_t excl[3], all[3], most;
   block_scan3<W>(mine, local_max, tmp, excl, all, &most);
+  // Past the scan's barrier every thread has consumed its loads of the
+  // counts matrix: take this workgroup's ticket now; its value is looked at
+  // only after the scatter, by when the atomic has long returned.
+  uint32_t my_ticket = 0u;
+  if (ticket != nullptr && threadIdx.x == 0)
+    my_ticket = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint32_t grand_total = all[0];
   // Router-filled counts that do not add up to N mean the matrix was not
   // zero on entry (or an id was out of range): report it in the status word
@@ -370,11 +377,7 @@ __device__ __forceinline__ void scatter_chunk(
   }
   if (ticket == nullptr) return;  // uniform
   __shared__ uint32_t is_last;
-  if (threadIdx.x == 0)
-    is_last = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                      static_cast<uint32_t>(nchunks - 1)
-                  ? 1u
-                  : 0u;
+  if (threadIdx.x == 0) is_last = my_ticket == static_cast<uint32_t>(nchunks - 1) ? 1u : 0u;
   __syncthreads();
   if (is_last == 0u) return;  // uniform
   uint32_t* clear = const_cast<uint32_t*>(counts);

@@ -82,7 +82,266 @@ __global__ __launch_bounds__(W * kWave) void index_scatter_kernel(
                    counts, N, E, chunk, nchunks, rounds, blockIdx.x, ticket);
 }
 
+// ---- ranked form: the router has ranked every slot ------------------------
+// moe_route_and_index's router recorded, per router workgroup (a fine row
+// of F slots), its count of slots per expert, and for each slot its rank
+// among the workgroup's earlier slots of the same expert, packed with the
+// expert id into restore_token_order. Chunk c (R fine rows) then places
+// slot i at
+//   start(e) + slots of e in earlier chunks + in earlier rows of this chunk
+//            + rank(i)
+// with no per-slot ballots and no running positions: one pass of loads,
+// two scans, a [rows, E] table of bases in LDS, one pass of stores.
+//
+// Expert work runs on quads of 4 consecutive experts (rows of counts have
+// a stride of E rounded up to 4, so a quad's counts are one 16-byte load):
+// the 16 lanes of a DPP row share a quad, lane p taking count rows p, p +
+// 16, ... and fine rows p and p + 16, and the sums and row scans run over
+// the 16 lanes in registers.
+constexpr int kRankedWaves = 16;
+constexpr int kRankedThreads = kRankedWaves * kWave;
+constexpr int kQuadLanes = 16;
+constexpr int kRankedFineLoads = kRankedMaxRowsPerChunk / kQuadLanes;   // 2
+constexpr int kRankedCountLoads = static_cast<int>(kMaxChunks) / kQuadLanes;  // 4
+constexpr int kRankedSlotsPerThread =
+    kRankedMaxRowsPerChunk * 256 / kRankedThreads;  // F <= 256
+
+// Zero n words from p with every thread of the workgroup: 16-byte stores
+// where p is 16-byte aligned, word stores for the rest.
+__device__ __forceinline__ void clear_words(uint32_t* p, int64_t n, int threads) {
+  int64_t head = 0;
+  if ((reinterpret_cast<uintptr_t>(p) & 15u) == 0u) {
+    const int64_t vecs = n / 4;
+    u32x4* v = reinterpret_cast<u32x4*>(p);
+    for (int64_t x = threadIdx.x; x < vecs; x += threads) v[x] = u32x4{0u, 0u, 0u, 0u};
+    head = vecs * 4;
+  }
+  for (int64_t x = head + threadIdx.x; x < n; x += threads) p[x] = 0u;
+}
+
+// Inclusive prefix over the 16 lanes of each DPP row (row_shr 1, 2, 4, 8).
+__device__ __forceinline__ uint32_t row_inclusive(uint32_t x) {
+  x += dpp_or_zero<kRowShr1, 0xF>(x);
+  x += dpp_or_zero<kRowShr2, 0xF>(x);
+  x += dpp_or_zero<kRowShr4, 0xF>(x);
+  x += dpp_or_zero<kRowShr8, 0xF>(x);
+  return x;
+}
+// Value of x in the last lane of the caller's row.
+__device__ __forceinline__ uint32_t row_last(uint32_t x) {
+  return static_cast<uint32_t>(__shfl(static_cast<int>(x), (lane_id() & ~15) + 15, kWave));
+}
+
+__global__ __launch_bounds__(kRankedThreads) void index_ranked_kernel(
+    uint32_t* __restrict__ order, uint32_t* __restrict__ starts, uint32_t* __restrict__ restore,
+    int32_t* __restrict__ expert_ids, uint32_t* __restrict__ stats,
+    uint32_t* __restrict__ scales_offset, uint32_t scale_align,
+    const uint32_t* __restrict__ fine, uint32_t* counts, uint32_t* ticket, int64_t N, int32_t E,
+    uint32_t F, uint32_t rows, uint32_t R, int64_t nchunks) {
+  __shared__ __align__(16) uint32_t table[kRankedMaxRowsPerChunk * kRankedMaxExperts];
+  __shared__ uint32_t tmp[4 * kRankedWaves];
+  const int lane = lane_id();
+  const int64_t c = blockIdx.x;
+  const uint32_t row0 = static_cast<uint32_t>(c) * R;
+  const uint32_t nrow = (rows - row0 < R) ? rows - row0 : R;
+  const int64_t c0 = static_cast<int64_t>(row0) * F;
+  const int64_t c1 =
+      (c0 + static_cast<int64_t>(nrow) * F < N) ? c0 + static_cast<int64_t>(nrow) * F : N;
+  const int32_t stride = ranked_stride(E);
+  const int q = static_cast<int>(threadIdx.x) / kQuadLanes;  // quad: experts 4q .. 4q + 3
+  const int part = static_cast<int>(threadIdx.x) % kQuadLanes;
+  const bool own = 4 * q < E;
+  const bool several = counts != nullptr;  // nchunks > 1
+
+  // 1. every load first: the chunk's packed slots, this lane's fine rows
+  // of its quad and, with several chunks, its count rows of its quad
+  uint32_t pk[kRankedSlotsPerThread];
+#pragma unroll
+  for (int j = 0; j < kRankedSlotsPerThread; ++j) {
+    const int64_t i = c0 + threadIdx.x + static_cast<int64_t>(j) * kRankedThreads;
+    pk[j] = i < c1 ? restore[i] : 0u;
+  }
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  u32x4 fv[kRankedFineLoads];
+#pragma unroll
+  for (int j = 0; j < kRankedFineLoads; ++j) {
+    const uint32_t r = static_cast<uint32_t>(part + j * kQuadLanes);
+    fv[j] = (own && r < nrow)
+                ? *reinterpret_cast<const u32x4*>(fine + static_cast<int64_t>(row0 + r) * stride +
+                                                  4 * q)
+                : zero4;
+  }
+  u32x4 cv[kRankedCountLoads];
+#pragma unroll
+  for (int j = 0; j < kRankedCountLoads; ++j) {
+    const int64_t cc = part + j * kQuadLanes;
+    cv[j] = (several && own && cc < nchunks)
+                ? *reinterpret_cast<const u32x4*>(counts + cc * stride + 4 * q)
+                : zero4;
+  }
+
+  // 2. per expert of the quad: exclusive prefix of this chunk's rows (row
+  // p + 16 j in lane p: a 16-lane scan per block of 16 rows), the chunk's
+  // total, and with several chunks the counts of all chunks and of the
+  // chunks before this one
+  uint32_t total[4], before[4], rowbase[kRankedFineLoads][4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t carry = 0;
+#pragma unroll
+    for (int j = 0; j < kRankedFineLoads; ++j) {
+      const uint32_t v = fv[j][k];
+      const uint32_t incl = row_inclusive(v);
+      rowbase[j][k] = carry + incl - v;
+      carry += row_last(incl);
+    }
+    if (several) {
+      uint32_t a = 0, b = 0;
+#pragma unroll
+      for (int j = 0; j < kRankedCountLoads; ++j) {
+        a += cv[j][k];
+        b += (part + j * kQuadLanes < c) ? cv[j][k] : 0u;
+      }
+      total[k] = row_last(row_inclusive(a));
+      before[k] = row_last(row_inclusive(b));
+    } else {
+      total[k] = carry;
+      before[k] = 0u;
+    }
+  }
+
+  // 3. block scan over the quads (lane 0 of each quad contributes its
+  // quad's sums): expert starts, active experts, padded rows, largest count
+  const bool owner = own && part == 0;
+  const bool want_pad = scales_offset != nullptr && c == 0;
+  uint32_t qsum = 0, qact = 0, qpad = 0, qmax = 0, pad[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    pad[k] = want_pad ? (total[k] + scale_align - 1u) / scale_align * scale_align : 0u;
+    qsum += total[k];
+    qact += total[k] != 0u ? 1u : 0u;
+    qpad += pad[k];
+    qmax = qmax > total[k] ? qmax : total[k];
+  }
+  const uint32_t mine[3] = {owner ? qsum : 0u, owner ? qact : 0u, owner ? qpad : 0u};
+  uint32_t excl[3], all[3], most;
+  block_scan3<kRankedWaves>(mine, owner ? qmax : 0u, tmp, excl, all, &most);
+  // past the scan's barrier every thread has consumed its loads of the
+  // counts matrix: take the ticket now, look at it after the scatter
+  uint32_t my_ticket = 0u;
+  if (several && threadIdx.x == 0)
+    my_ticket = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int quad_lane0 = lane & ~(kQuadLanes - 1);
+  const uint32_t quad_start =
+      static_cast<uint32_t>(__shfl(static_cast<int>(excl[0]), quad_lane0, kWave));
+  const uint32_t grand_total = all[0];
+  // counts that do not add up to N: the counts matrix was not zero on entry
+  if (several && c == 0 && threadIdx.x == 0 && grand_total != static_cast<uint32_t>(N))
+    __hip_atomic_store(ticket + 1, static_cast<uint32_t>(MOE_STATUS_COUNTS_MISMATCH),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint32_t start[4];
+  {
+    uint32_t run = quad_start;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      start[k] = run;
+      run += total[k];
+    }
+  }
+
+  // 4. bases of this lane's rows: one 16-byte LDS store per row
+#pragma unroll
+  for (int j = 0; j < kRankedFineLoads; ++j) {
+    const uint32_t r = static_cast<uint32_t>(part + j * kQuadLanes);
+    if (own && r < nrow) {
+      u32x4 b;
+      b.x = start[0] + before[0] + rowbase[j][0];
+      b.y = start[1] + before[1] + rowbase[j][1];
+      b.z = start[2] + before[2] + rowbase[j][2];
+      b.w = start[3] + before[3] + rowbase[j][3];
+      *reinterpret_cast<u32x4*>(table + r * stride + 4 * q) = b;
+    }
+  }
+
+  // 5. chunk 0: compacted active experts, CSR starts, stats, aligned offsets
+  if (c == 0) {
+    if (owner) {
+      uint32_t slot = excl[1], padded = excl[2];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (4 * q + k < E && total[k] != 0u && slot < static_cast<uint32_t>(E)) {
+          expert_ids[slot] = 4 * q + k;
+          starts[slot] = start[k];
+          if (want_pad) scales_offset[slot] = padded;
+          ++slot;
+        }
+        padded += pad[k];
+      }
+    }
+    const uint32_t n_active = all[1];
+    for (int x = static_cast<int>(n_active) + static_cast<int>(threadIdx.x); x <= E;
+         x += kRankedThreads) {
+      starts[x] = grand_total;
+      if (x < E) expert_ids[x] = -1;
+      if (want_pad) scales_offset[x] = all[2];
+    }
+    if (threadIdx.x == 0) {
+      stats[0] = most;
+      stats[1] = n_active;
+    }
+  }
+  __syncthreads();
+
+  // 6. every slot to its place
+#pragma unroll
+  for (int j = 0; j < kRankedSlotsPerThread; ++j) {
+    const int64_t i = c0 + threadIdx.x + static_cast<int64_t>(j) * kRankedThreads;
+    if (i >= c1) break;
+    const uint32_t ex = pk[j] & ((1u << kPackedExpertBits) - 1u);
+    const uint32_t rank = pk[j] >> kPackedExpertBits;
+    const uint32_t r = static_cast<uint32_t>(i - c0) / F;
+    if (ex < static_cast<uint32_t>(E) && r < nrow) {  // always, for the router's slots
+      const uint32_t pos = table[r * stride + ex] + rank;
+      if (static_cast<int64_t>(pos) < N) order[pos] = static_cast<uint32_t>(i);
+      restore[i] = pos;
+    } else {
+      restore[i] = 0xFFFFFFFFu;
+    }
+  }
+
+  // 7. several chunks: the workgroup that drew the last ticket clears the
+  // counts matrix and the ticket for the next call (a read-before-write
+  // order only, as in the chunked form)
+  if (!several) return;  // uniform
+  __shared__ uint32_t is_last;
+  if (threadIdx.x == 0) is_last = my_ticket == static_cast<uint32_t>(nchunks - 1) ? 1u : 0u;
+  __syncthreads();
+  if (is_last == 0u) return;  // uniform
+  clear_words(counts, nchunks * stride, kRankedThreads);
+  if (threadIdx.x == 0)
+    __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace
+
+moe_status_t launch_indices_ranked(uint32_t* order, uint32_t* starts, uint32_t* restore,
+                                   int32_t* expert_ids, uint32_t* stats, uint32_t* scales,
+                                   uint32_t align, int64_t N, int32_t E, const uint32_t* fine,
+                                   uint32_t* counts, uint32_t* ticket, const RankedPlan& plan,
+                                   hipStream_t stream) {
+  if (!plan.ok || E > kRankedMaxExperts || plan.R > kRankedMaxRowsPerChunk || plan.F > 256 ||
+      plan.nchunks < 1 || plan.nchunks > kMaxChunks)
+    return MOE_ERR_UNSUPPORTED;
+  // 16-byte loads of the fine rows and the counts matrix
+  if ((reinterpret_cast<uintptr_t>(fine) & 15u) != 0u ||
+      (plan.nchunks > 1 && (reinterpret_cast<uintptr_t>(counts) & 15u) != 0u))
+    return MOE_ERR_ALIGNMENT;
+  hipLaunchKernelGGL(index_ranked_kernel, dim3(static_cast<uint32_t>(plan.nchunks)),
+                     dim3(kRankedThreads), 0, stream, order, starts, restore, expert_ids, stats,
+                     scales, align, fine, plan.nchunks > 1 ? counts : nullptr, ticket, N, E,
+                     plan.F, plan.rows, plan.R, plan.nchunks);
+  return check_launch();
+}
 
 namespace {
 template <int W>

@@ -56,4 +56,54 @@ int64_t route_index_max_tokens(int32_t E) {
   return waves * (kWave / lanes_per_token);
 }
 
+// Two tokens per wave where it pays (measured, 20 launches per HIP graph):
+// E = 64 ... 256, groups of at least 2 * E / 64 experts (whole lanes),
+// K <= 32 (slot k of a token lives in lane k of its half), T >= 8192, or
+// >= 4096 when the router also records the index step's counts.
+bool router_two_tokens_per_wave(int64_t T, int32_t E, int32_t K, int32_t G, bool counting) {
+  return (E & (E - 1)) == 0 && E >= kWave && E <= 256 && G <= 32 && K <= kWave / 2 &&
+         T >= (counting ? 4096 : 8192);
+}
+
+int32_t router_block_tokens(int64_t T, int32_t E, int32_t K, int32_t G, bool counting) {
+  if ((E & (E - 1)) != 0) return kWavesPerBlock;  // general form: one token per wave
+  if (router_two_tokens_per_wave(T, E, K, G, counting)) return kWavesPerBlock * 2;
+  const int32_t lanes_per_token = E < kWave ? E : kWave;
+  return kWavesPerBlock * (kWave / lanes_per_token);
+}
+
+// Fine rows of the ranked form: one per router workgroup (F = its slots),
+// at most kRankedMaxRowsPerChunk per index chunk and kMaxChunks chunks, so
+// the chunk's [rows, E] table of bases fits LDS. Index chunks of about 1024
+// slots (2048 measured no faster at E = 8 and 256), or fewer, larger chunks
+// when that would exceed kMaxChunks.
+RankedPlan plan_ranked(int64_t T, int32_t K, int32_t E, int32_t G) {
+  RankedPlan p{false, 0, 0, 0, 0};
+  if (T < 1 || E < 1 || E > kRankedMaxExperts) return p;
+  const int64_t tpb = router_block_tokens(T, E, K, G, true);
+  const int64_t F = tpb * K;
+  const int64_t rows = (T + tpb - 1) / tpb;
+  if (F > 256 || rows > kMaxChunks * kRankedMaxRowsPerChunk) return p;
+  int64_t R = 1024 / F;
+  if (R < 1) R = 1;
+  if (R > kRankedMaxRowsPerChunk) R = kRankedMaxRowsPerChunk;
+  if ((rows + R - 1) / R > kMaxChunks) R = (rows + kMaxChunks - 1) / kMaxChunks;
+  p.F = static_cast<uint32_t>(F);
+  p.rows = static_cast<uint32_t>(rows);
+  p.R = static_cast<uint32_t>(R);
+  p.nchunks = (rows + R - 1) / R;
+  // With a single chunk the one-workgroup index step of the chunked form
+  // was as fast as the ranked one, and the ranking costs the router about
+  // a microsecond (measured at T = 128, E = 256): several chunks only.
+  p.ok = p.nchunks > 1;
+  return p;
+}
+
+// Router workgroups take at least kWavesPerBlock tokens each.
+int64_t ranked_fine_rows_bound(int64_t T) {
+  const int64_t rows = (T + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int64_t cap = kMaxChunks * kRankedMaxRowsPerChunk;
+  return rows < cap ? rows : cap;
+}
+
 }  // namespace moe

@@ -126,13 +126,8 @@ moe_status_t launch_router(int32_t* idx, void* w, const void* s, const void* b,
                            int32_t K, int32_t G, int32_t TG, int32_t norm, float scale,
                            int32_t mode, RouterHist hist, hipStream_t stream) {
   if ((E & (E - 1)) == 0) {
-    // two tokens per wave where it pays (measured, 20 launches per HIP
-    // graph): E = 64 ... 256, groups of at least 2 * E / 64 experts (whole
-    // lanes), K <= 32 (slot k of a token lives in lane k of its half),
-    // T >= 8192, or >= 4096 when the router also fills the index histogram
-    const bool wide = E >= kWave && E <= 256 && G <= 32 && K <= kWave / 2 &&
-                      T >= (hist.counts != nullptr ? 4096 : 8192);
-    if (wide)
+    const bool counting = hist.counts != nullptr || hist.fine != nullptr;
+    if (router_two_tokens_per_wave(T, E, K, G, counting))
       return dispatch_router<RouterWideLaunch>(sd, bd, fn, E, idx, w, s, b, T, K, G, TG, norm,
                                                scale, mode, hist, stream);
     return dispatch_router<RouterLaunch>(sd, bd, fn, E, idx, w, s, b, T, K, G, TG, norm, scale,

@@ -452,7 +452,52 @@ __device__ __forceinline__ void route_tokens(
   // slot order, then wave 0 groups equal keys (peer masks from ballots) and
   // one lane per distinct key issues the global add. A workgroup holds at
   // most 256 slots and a chunk at least 256, so the offset is 0 or 1.
-  if (hist.counts != nullptr) {  // uniform
+  if (hist.fine != nullptr) {  // uniform: ranked form of the index step
+    // Each slot's expert goes to LDS in slot order; wave 0 then walks the
+    // workgroup's slots 64 at a time in that order, with a running count
+    // per expert in LDS: a slot's rank is the count before its round plus
+    // its peers in lower lanes (ballot peer masks), the lowest peer adds the
+    // round's count, to the running count and (several chunks) to its
+    // chunk's row of the counts (relaxed atomics: integer sums do not depend
+    // on their order). Stores (rank << 10) | expert for the slot, then the
+    // workgroup's row of counts.
+    constexpr int kThreads = WPB * kWave;
+    __shared__ uint32_t slot_expert[kThreads];
+    __shared__ uint32_t running[kRankedMaxExperts];
+    const int64_t t1 = (t0 + WPB * TPW < T) ? t0 + WPB * TPW : T;
+    const int nslots = static_cast<int>((t1 - t0) * K);
+    if (slot) slot_expert[(t - t0) * K + sub] = my_id;
+    __syncthreads();
+    if (wave == 0) {
+      for (int x = lane; x < E; x += kWave) running[x] = 0u;
+      __builtin_amdgcn_wave_barrier();
+      int nb = 0;
+      while ((1 << nb) < E) ++nb;
+      uint32_t* packed = hist.packed + static_cast<uint64_t>(t0) * K;
+      const int32_t stride = ranked_stride(E);
+      uint32_t* crow = hist.counts == nullptr
+                           ? nullptr
+                           : hist.counts + static_cast<uint64_t>(block / hist.rows_per_chunk) *
+                                               stride;
+      for (int r = 0; r < nslots; r += kWave) {
+        const bool ok = r + lane < nslots;
+        const uint32_t e = ok ? slot_expert[r + lane] : 0u;
+        const uint64_t peers = match_any(e, nb, __ballot(ok));
+        const uint32_t before = ok ? running[e] : 0u;
+        __builtin_amdgcn_wave_barrier();  // every lane reads before the update
+        if (ok && (__ffsll(static_cast<unsigned long long>(peers)) - 1) == lane) {
+          const uint32_t n = static_cast<uint32_t>(__popcll(peers));
+          running[e] = before + n;
+          if (crow != nullptr)  // one lane per distinct expert of the round
+            __hip_atomic_fetch_add(crow + e, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (ok) packed[r + lane] = ((before + popc_below(peers)) << kPackedExpertBits) | e;
+        __builtin_amdgcn_wave_barrier();
+      }
+      uint32_t* row = hist.fine + static_cast<uint64_t>(block) * stride;
+      for (int x = lane; x < stride; x += kWave) row[x] = x < E ? running[x] : 0u;
+    }
+  } else if (hist.counts != nullptr) {  // uniform: chunked form
     constexpr int kThreads = WPB * kWave;
     __shared__ uint32_t keys[kThreads];
     const int64_t t1 = (t0 + WPB * TPW < T) ? t0 + WPB * TPW : T;

@@ -11,14 +11,14 @@
 #include "common.hpp"
 
 namespace {
-int g_router = 0, g_indices = 0, g_route_index = 0, g_finalize = 0;
+int g_router = 0, g_indices = 0, g_route_index = 0, g_finalize = 0, g_ranked = 0;
 int g_fail = 0;
 moe::IndexPlan g_last_plan{};
 bool g_last_counts_ready = false;
 const void* g_last_counts = nullptr;
 
-void reset() { g_router = g_indices = g_route_index = g_finalize = 0; }
-int launches() { return g_router + g_indices + g_route_index + g_finalize; }
+void reset() { g_router = g_indices = g_route_index = g_finalize = g_ranked = 0; }
+int launches() { return g_router + g_indices + g_route_index + g_finalize + g_ranked; }
 
 #define EXPECT(cond)                                                \
   do {                                                              \
@@ -47,6 +47,20 @@ moe_status_t launch_indices(uint32_t*, uint32_t*, uint32_t*, int32_t*, uint32_t*
   g_last_counts_ready = counts_ready;
   g_last_counts = workspace;
   ++g_indices;
+  return MOE_OK;
+}
+moe_status_t launch_indices_ranked(uint32_t*, uint32_t*, uint32_t*, int32_t*, uint32_t*,
+                                   uint32_t*, uint32_t, int64_t N, int32_t E, const uint32_t* fine,
+                                   uint32_t* counts, uint32_t* ticket, const RankedPlan& plan,
+                                   hipStream_t) {
+  EXPECT(plan.ok && N >= 1 && E >= 1 && E <= kRankedMaxExperts && fine != nullptr);
+  EXPECT(plan.nchunks >= 1 && plan.nchunks <= kMaxChunks && plan.R <= kRankedMaxRowsPerChunk);
+  EXPECT(static_cast<int64_t>(plan.rows) * plan.F >= N);
+  EXPECT((plan.nchunks > 1) == (counts != nullptr) && ticket != nullptr);
+  g_last_plan.nchunks = plan.nchunks;
+  g_last_counts_ready = true;
+  g_last_counts = counts;
+  ++g_ranked;
   return MOE_OK;
 }
 moe_status_t launch_route_index(int32_t*, void*, const void*, const void*, moe_dtype_t,
@@ -169,9 +183,25 @@ int main() {
   EXPECT(route_index(INT64_MAX, 256, 8, P, need) == MOE_ERR_INVALID_ARG);
   EXPECT(launches() == 0);
   EXPECT(route_index(16, 256, 8, P, 256) == MOE_OK && g_route_index == 1 && g_router == 0);
-  EXPECT(route_index(8192, 256, 8, P, need) == MOE_OK && g_router == 1 && g_indices == 1);
+  // ranked form: router, then the ranked index step over several chunks
+  EXPECT(route_index(8192, 256, 8, P, need) == MOE_OK && g_router == 1 && g_ranked == 1);
   EXPECT(g_last_counts_ready && g_last_plan.nchunks > 1);
   EXPECT(g_last_counts == static_cast<const char*>(P) + 256);  // the matrix follows the header
+  // one index chunk: the chunked form's single-workgroup index step
+  reset();
+  EXPECT(route_index(128, 256, 8, P, moe_route_and_index_workspace_size(128, 8, 256)) == MOE_OK);
+  EXPECT(g_ranked == 0 && g_indices == 1 && g_last_plan.nchunks == 1 && !g_last_counts_ready);
+  // a workspace that is not 16-byte aligned: chunked form
+  reset();
+  EXPECT(route_index(8192, 256, 8, static_cast<char*>(P) + 4, need) == MOE_OK);
+  EXPECT(g_ranked == 0 && g_indices == 1 && g_last_counts_ready);
+  // E above 256: chunked form
+  reset();
+  const size_t need512 = moe_route_and_index_workspace_size(8192, 8, 512);
+  EXPECT(moe_route_and_index(I, P, U, U, U, I, U, nullptr, 0, P, P, MOE_DTYPE_F32, MOE_DTYPE_F32,
+                             MOE_SCORE_NONE, 8192, 512, 8, 8, 4, 1, 2.5f, MOE_GROUP_TOP2_SUM, P,
+                             need512, nullptr) == MOE_OK);
+  EXPECT(g_router == 1 && g_indices == 1 && g_ranked == 0 && g_last_counts_ready);
 
   // finalize
   reset();

@@ -44,6 +44,42 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, fn), fn
 
 
+PROBE_HEADER = os.path.join(ROOT, "include", "moe_probe.h")
+
+
+@pytest.fixture(scope="module")
+def probe_lib():
+    from permutation_group_limited_amd import probe
+    if not os.path.exists(probe._LIB_PATH):
+        from permutation_group_limited_amd import build
+        build.build()
+    return probe.load_library()
+
+
+def test_probe_library_exports_its_header(probe_lib):
+    src = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(moe_probe_\w+)\s*\(", src)))
+    assert names == ["moe_probe_gather", "moe_probe_read", "moe_probe_write"]
+    for fn in names:
+        assert hasattr(probe_lib, fn), fn
+
+
+def test_probe_validation(probe_lib):
+    # sizes that are not whole waves, missing pointers, misalignment: nothing launched
+    assert probe_lib.moe_probe_read(FAKE, 8191, FAKE, None) == INVALID
+    assert probe_lib.moe_probe_read(None, 8192, FAKE, None) == INVALID
+    assert probe_lib.moe_probe_read(FAKE_ODD, 8192, FAKE, None) == ALIGNMENT
+    assert probe_lib.moe_probe_read(FAKE, (1 << 40) + 8192, FAKE, None) == INVALID
+    assert probe_lib.moe_probe_read(None, 0, None, None) == OK
+    assert probe_lib.moe_probe_write(FAKE, 1000, 0, None) == INVALID
+    assert probe_lib.moe_probe_write(FAKE_ODD, 1024, 0, None) == ALIGNMENT
+    assert probe_lib.moe_probe_gather(FAKE, FAKE, -1, 8, 14336, FAKE, None) == INVALID
+    assert probe_lib.moe_probe_gather(FAKE, FAKE, 4, 0, 14336, FAKE, None) == INVALID
+    assert probe_lib.moe_probe_gather(FAKE, FAKE, 4, 8, 14330, FAKE, None) == INVALID
+    assert probe_lib.moe_probe_gather(FAKE_ODD, FAKE, 4, 8, 14336, FAKE, None) == ALIGNMENT
+    assert probe_lib.moe_probe_gather(None, None, 0, 8, 14336, None, None) == OK
+
+
 def test_status_strings(lib):
     for code in range(6):
         assert lib.moe_status_string(code)
@@ -222,15 +258,21 @@ def route_index(lib, T=16, E=256, K=8, G=8, TG=4, fn=0, sd=0, bd=0, mode=0, ws=F
 
 def test_route_and_index_workspace_size(lib):
     ws = lib.moe_route_and_index_workspace_size
-    # a counter (256 bytes padded) and, for several index chunks, the counts
-    assert ws(128, 8, 256) == 256
-    assert ws(8192, 8, 256) == 256 + lib.moe_create_indices_workspace_size(65536, 256)
-    assert ws(8192, 8, 256) > 256
-    assert ws(100, 6, 160) == 256
-    # after the router has counted: one workgroup up to 4 rounds of 1024
-    # slots, past that room for the counts of up to 64 chunks
-    assert ws(512, 8, 256) == 256 and ws(513, 8, 256) == 256 + 256 * 4 * 64
-    assert ws(2048, 2, 8) == 256 and ws(2049, 2, 8) == 256 + 8 * 4 * 64
+
+    def ranked(T, E):  # header, 64 rows of counts, fine rows (stride E rounded up to 4)
+        Ep = (E + 3) // 4 * 4
+        return 256 + 64 * Ep * 4 + min((T + 3) // 4, 2048) * Ep * 4
+
+    # one launch (T <= 16 at E = 256, 128 at E = 8): the 256-byte header only
+    assert ws(16, 8, 256) == 256 and ws(128, 2, 8) == 256
+    # two launches, E <= 256: header, counts matrix and the router's fine rows
+    assert ws(17, 8, 256) == ranked(17, 256)
+    assert ws(128, 8, 256) == ranked(128, 256)
+    assert ws(8192, 8, 256) == ranked(8192, 256)
+    assert ws(100, 6, 160) == ranked(100, 160)
+    assert ws(4096, 2, 8) == ranked(4096, 8)
+    assert ws(1 << 20, 8, 256) == ranked(1 << 20, 256)  # fine rows capped at 2048
+    # E > 256 (chunked form only): the counts matrix once several chunks are possible
     assert ws(256, 8, 512) == 256 and ws(257, 8, 512) == 256 + 512 * 4 * 64
     # the case that once shrank: 8200 tokens needed less than 8192
     assert ws(8200, 8, 256) >= ws(8192, 8, 256)

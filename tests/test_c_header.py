@@ -38,12 +38,13 @@ def _cc():
 
 
 @pytest.mark.skipif(_cc() is None, reason="no C compiler")
+@pytest.mark.parametrize("header", ["moe_route.h", "moe_probe.h"])
 @pytest.mark.parametrize("lang,std", [("c", "-std=c99"), ("c++", "-std=c++17")])
-def test_header_compiles(lang, std):
+def test_header_compiles(lang, std, header):
     with tempfile.TemporaryDirectory() as d:
         src = os.path.join(d, "h." + ("c" if lang == "c" else "cc"))
         with open(src, "w") as f:
-            f.write('#include "moe_route.h"\n')
+            f.write('#include "%s"\n' % header)
         r = subprocess.run([_cc(), "-x", lang, std, "-Wall", "-Wextra", "-Werror", "-pedantic",
                             "-fsyntax-only", "-I", INCLUDE, src], capture_output=True, text=True)
         assert r.returncode == 0, r.stderr
@@ -67,5 +68,6 @@ def test_c_program_links_and_validates():
         assert r.returncode == 0, r.stderr
         lines = r.stdout.split()
     expect_ws = binding.moe_create_indices_workspace_size(65536, 256)
-    assert lines[-4:] == ["0", str(expect_ws), "256", "1"]
+    expect_ri = binding.moe_route_and_index_workspace_size(128, 8, 256)
+    assert lines[-4:] == ["0", str(expect_ws), str(expect_ri), "1"]
     assert "INVALID" in r.stdout.upper()

@@ -68,9 +68,15 @@ def workspace(T, K, E):
     return torch.zeros(n // 4, dtype=torch.int32, device=DEV)
 
 
-def assert_zero(ws, what=""):
-    nz = int(torch.count_nonzero(ws).item())
-    assert nz == 0, "workspace not left zero (%d words set) %s" % (nz, what)
+def zero_part(ws, E):
+    """The header and the counts matrix: the part of the workspace every
+    call leaves zero (the rest is scratch)."""
+    return ws[:(256 + 64 * ((E + 3) // 4 * 4) * 4) // 4]
+
+
+def assert_zero(ws, E, what=""):
+    nz = int(torch.count_nonzero(zero_part(ws, E)).item())
+    assert nz == 0, "workspace header / counts not left zero (%d words set) %s" % (nz, what)
 
 
 def fused(x, b, K, G, TG, norm, scale, fn="none", mode=0, align=0, ws=None):
@@ -80,7 +86,7 @@ def fused(x, b, K, G, TG, norm, scale, fn="none", mode=0, align=0, ws=None):
     ws = workspace(T, K, E) if ws is None else ws
     launch(o, x.to(DEV), b.to(DEV), ws, G, TG, norm, scale, FNS[fn][0], mode, align)
     torch.cuda.synchronize()
-    assert_zero(ws)
+    assert_zero(ws, E)
     return o.host()
 
 
@@ -175,7 +181,10 @@ def test_workload_shapes(name, T, from_logits):
                                         (4099, 256, 8, 4, 40),
                                         (5000, 1024, 16, 4, 8), (2500, 8, 1, 1, 8),
                                         (100, 160, 8, 3, 6), (4096, 160, 8, 3, 6),
-                                        (777, 20, 4, 3, 6), (3000, 1000, 8, 4, 8)])
+                                        (777, 20, 4, 3, 6), (3000, 1000, 8, 4, 8),
+                                        # ranked form with E not a multiple of 4
+                                        # (rows of counts padded to 8 and 12)
+                                        (1500, 6, 2, 1, 2), (900, 10, 5, 2, 3)])
 @pytest.mark.parametrize("levels", [0, 3])
 def test_random_shapes(T, E, G, TG, K, levels):
     log("route_and_index random", T, E, G, TG, K, levels)
@@ -243,7 +252,7 @@ def test_back_to_back_calls_share_the_counter():
         launch(o, x.to(DEV), b.to(DEV), ws, 8, 4, True, 2.5, binding.SCORE_NONE)
         cases.append((x, b, o))
     torch.cuda.synchronize()
-    assert_zero(ws)
+    assert_zero(ws, wk.E)
     for x, b, o in cases:
         check_against_oracle(o.host(), x, b, wk.K, 8, 4, True, 2.5)
 
@@ -284,7 +293,7 @@ def test_graph_replay(name, T):
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        assert_zero(ws, "after replay %d" % rep)
+        assert_zero(ws, wk.E, "after replay %d" % rep)
         check_same(o.host(), ref)
 
 
@@ -309,7 +318,7 @@ def test_huge_batch_matches_separate():
     binding.moe_create_indices_aligned(so.order, so.starts, so.restore, so.eids, so.stats,
                                        so.idx, ws2, so.scales, 16)
     torch.cuda.synchronize()
-    assert_zero(ws)
+    assert_zero(ws, E)
     for name in ("idx", "order", "restore", "starts", "eids", "stats", "scales"):
         assert torch.equal(getattr(fo, name), getattr(so, name)), name
     assert torch.equal(fo.w.view(torch.int32), so.w.view(torch.int32))
@@ -332,7 +341,7 @@ def test_workspace_sized_for_a_larger_batch():
         launch(o, x.to(DEV), b.to(DEV), ws, G, TG, True, 2.5, binding.SCORE_NONE)
         cases.append((x, b, o))
     torch.cuda.synchronize()
-    assert_zero(ws)
+    assert_zero(ws, E)
     for x, b, o in cases:
         check_against_oracle(o.host(), x, b, K, G, TG, True, 2.5)
 
@@ -351,13 +360,14 @@ def test_dirty_workspace_is_reported():
     ws = workspace(T, K, E)
     status = binding.ROUTE_INDEX_STATUS_OFFSET // 4
     header = 256 // 4
-    ws[header:] = 1  # every count off by one
+    ws[header:] = 1  # every count off by one (and the scratch past the matrix dirty too)
     o = Outputs(T, E, K, torch.float32, False)
     launch(o, x.to(DEV), b.to(DEV), ws, wk.n_groups, wk.topk_group, True, wk.scale,
            binding.SCORE_NONE)
     torch.cuda.synchronize()
     assert int(ws[status].item()) == binding.STATUS_COUNTS_MISMATCH
-    rest = torch.cat([ws[:status], ws[status + 1:]])
+    zp = zero_part(ws, E)
+    rest = torch.cat([zp[:status], zp[status + 1:]])
     assert int(torch.count_nonzero(rest).item()) == 0, "matrix or ticket not cleared"
     # the router's own outputs do not depend on the workspace
     got = o.host()
@@ -368,3 +378,21 @@ def test_dirty_workspace_is_reported():
     got = fused(x, b, K, wk.n_groups, wk.topk_group, True, wk.scale, ws=ws)
     assert int(ws[status].item()) == 0
     check_against_oracle(got, x, b, K, wk.n_groups, wk.topk_group, True, wk.scale)
+
+
+@pytest.mark.parametrize("name,T", [("dsv3", 8192), ("decode", 128), ("mixtral", 4096)])
+def test_workspace_4_byte_aligned(name, T):
+    """A workspace that is 4-byte but not 16-byte aligned takes the chunked
+    form (the ranked form moves rows of counts in 16-byte pieces): same
+    outputs, header and counts left zero."""
+    wk = wl.WORKLOADS[name].with_tokens(T)
+    log("route_and_index 4-byte aligned workspace", wk.describe())
+    x, b = wl.make_scores(wk), wl.make_bias(wk)
+    n = binding.moe_route_and_index_workspace_size(wk.T, wk.K, wk.E) // 4
+    base = torch.zeros(n + 4, dtype=torch.int32, device=DEV)
+    ws = base[1:1 + n]
+    assert ws.data_ptr() % 16 == 4
+    args = (wk.K, wk.n_groups, wk.topk_group, wk.norm_weights, wk.scale)
+    got = fused(x, b, *args, ws=ws)
+    check_against_oracle(got, x, b, *args)
+    check_same(got, fused(x, b, *args))
