@@ -280,8 +280,9 @@ size_t moe_route_and_index_workspace_size(int64_t T, int32_t K, int32_t E);
  *     (16 tokens for E in 64..256, 8 for 512, 4 for 1024, 64 * 16 / E
  *     below 64): one launch, that workgroup routing every token and then
  *     building the index outputs;
- *   - otherwise two launches. For E <= 256, batches of at most 2048
- *     router workgroups and a 16-byte aligned workspace (ranked form),
+ *   - otherwise two launches. For E <= 256, batches of more than one
+ *     index chunk and at most 32768 router workgroups, and a 16-byte
+ *     aligned workspace (ranked form),
  *     the router also ranks each slot
  *     among the earlier slots of its workgroup with the same expert and
  *     records each workgroup's count per expert (scratch in the workspace

@@ -262,7 +262,7 @@ moe_status_t moe_route_and_index(int32_t* expert_indices, void* expert_weights,
     // matrix when there are several chunks); the index step places each
     // slot from those alone
     uint32_t* fine = counts + ranked_counts_bytes(E) / sizeof(uint32_t);
-    uint32_t* coarse = rp.nchunks > 1 ? counts : nullptr;
+    uint32_t* coarse = counts;  // the ranked form always has several chunks
     const moe_status_t rs = launch_router(
         expert_indices, expert_weights, router_input, expert_bias, input_dtype, bias_dtype,
         static_cast<int32_t>(score_fn), T, E, K, n_groups, topk_group, norm_weights ? 1 : 0,

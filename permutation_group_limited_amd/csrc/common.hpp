@@ -180,7 +180,8 @@ struct RankedPlan {
   uint32_t R;
   int64_t nchunks;
 };
-constexpr uint32_t kRankedMaxRowsPerChunk = 32;
+constexpr uint32_t kRankedMaxRowsPerChunk = 512;
+constexpr uint32_t kRankedBlockRows = 32;  // rows of the table of bases held in LDS at a time
 // Rows of counts in the ranked form have a stride of E rounded up to a
 // multiple of 4 (padding entries zero), so that they move in 16-byte pieces.
 __host__ __device__ constexpr int32_t ranked_stride(int32_t E) { return (E + 3) & ~3; }

@@ -73,10 +73,10 @@ int32_t router_block_tokens(int64_t T, int32_t E, int32_t K, int32_t G, bool cou
 }
 
 // Fine rows of the ranked form: one per router workgroup (F = its slots),
-// at most kRankedMaxRowsPerChunk per index chunk and kMaxChunks chunks, so
-// the chunk's [rows, E] table of bases fits LDS. Index chunks of about 1024
-// slots (2048 measured no faster at E = 8 and 256), or fewer, larger chunks
-// when that would exceed kMaxChunks.
+// at most kRankedMaxRowsPerChunk per index chunk and kMaxChunks chunks (the
+// index workgroup walks its rows kRankedBlockRows at a time). Index chunks
+// of about 1024 slots (2048 measured no faster at E = 8 and 256), or fewer,
+// larger chunks when that would exceed kMaxChunks.
 RankedPlan plan_ranked(int64_t T, int32_t K, int32_t E, int32_t G) {
   RankedPlan p{false, 0, 0, 0, 0};
   if (T < 1 || E < 1 || E > kRankedMaxExperts) return p;

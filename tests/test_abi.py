@@ -261,7 +261,7 @@ def test_route_and_index_workspace_size(lib):
 
     def ranked(T, E):  # header, 64 rows of counts, fine rows (stride E rounded up to 4)
         Ep = (E + 3) // 4 * 4
-        return 256 + 64 * Ep * 4 + min((T + 3) // 4, 2048) * Ep * 4
+        return 256 + 64 * Ep * 4 + min((T + 3) // 4, 64 * 512) * Ep * 4
 
     # one launch (T <= 16 at E = 256, 128 at E = 8): the 256-byte header only
     assert ws(16, 8, 256) == 256 and ws(128, 2, 8) == 256
@@ -271,7 +271,7 @@ def test_route_and_index_workspace_size(lib):
     assert ws(8192, 8, 256) == ranked(8192, 256)
     assert ws(100, 6, 160) == ranked(100, 160)
     assert ws(4096, 2, 8) == ranked(4096, 8)
-    assert ws(1 << 20, 8, 256) == ranked(1 << 20, 256)  # fine rows capped at 2048
+    assert ws(1 << 20, 8, 256) == ranked(1 << 20, 256)  # fine rows capped at 64 * 512
     # E > 256 (chunked form only): the counts matrix once several chunks are possible
     assert ws(256, 8, 512) == 256 and ws(257, 8, 512) == 256 + 512 * 4 * 64
     # the case that once shrank: 8200 tokens needed less than 8192
