@@ -139,7 +139,9 @@ __global__ __launch_bounds__(kRankedThreads) void index_ranked_kernel(
     uint32_t* __restrict__ scales_offset, uint32_t scale_align,
     const uint32_t* __restrict__ fine, uint32_t* counts, uint32_t* ticket, int64_t N, int32_t E,
     uint32_t F, uint32_t rows, uint32_t R, int64_t nchunks) {
-  __shared__ __align__(16) uint32_t table[kRankedBlockRows * kRankedMaxExperts];
+  // rows of the table padded by 4 words: the 16 lanes of a quad write 16
+  // rows, which would otherwise all fall on the same LDS banks
+  __shared__ __align__(16) uint32_t table[kRankedBlockRows * (kRankedMaxExperts + 4)];
   __shared__ uint32_t tmp[4 * kRankedWaves];
   const int lane = lane_id();
   const int64_t c = blockIdx.x;
@@ -149,6 +151,7 @@ __global__ __launch_bounds__(kRankedThreads) void index_ranked_kernel(
   const int64_t c1 =
       (c0 + static_cast<int64_t>(nrow) * F < N) ? c0 + static_cast<int64_t>(nrow) * F : N;
   const int32_t stride = ranked_stride(E);
+  const int32_t tstride = stride + 4;  // row stride of the LDS table
   const int q = static_cast<int>(threadIdx.x) / kQuadLanes;  // quad: experts 4q .. 4q + 3
   const int part = static_cast<int>(threadIdx.x) % kQuadLanes;
   const bool own = 4 * q < E;
@@ -284,7 +287,7 @@ __global__ __launch_bounds__(kRankedThreads) void index_ranked_kernel(
         v.y = base[j][1];
         v.z = base[j][2];
         v.w = base[j][3];
-        *reinterpret_cast<u32x4*>(table + r * stride + 4 * q) = v;
+        *reinterpret_cast<u32x4*>(table + r * tstride + 4 * q) = v;
       }
     }
     __syncthreads();
@@ -296,7 +299,7 @@ __global__ __launch_bounds__(kRankedThreads) void index_ranked_kernel(
       const uint32_t rank = pk[j] >> kPackedExpertBits;
       const uint32_t r = static_cast<uint32_t>(i - s0) / F;
       if (ex < static_cast<uint32_t>(E) && r < brows) {  // always, for the router's slots
-        const uint32_t pos = table[r * stride + ex] + rank;
+        const uint32_t pos = table[r * tstride + ex] + rank;
         if (static_cast<int64_t>(pos) < N) order[pos] = static_cast<uint32_t>(i);
         restore[i] = pos;
       } else {
