@@ -9,9 +9,11 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * Memory. Every tensor argument is a plain pointer to DEVICE memory owned by
- * the caller, densely packed in row-major order (no strides). The library
- * never allocates, frees or retains memory and keeps no state between calls.
- * Scratch space, where needed, is a caller-provided device workspace.
+ * the caller, densely packed in row-major order (no strides). The entry
+ * points never allocate, free or retain memory; scratch space, where
+ * needed, is a caller-provided device workspace. The only memory the
+ * library owns is the fixed device array of moe_create_indices_no_alloc
+ * (one per GPU, for the life of the process).
  *
  * Streams. `stream` is a hipStream_t passed as void* (NULL = the legacy null
  * stream of the current device). All work is enqueued asynchronously on that
@@ -136,10 +138,17 @@ typedef enum {
  * The router with the scores computed on the fly from logits: the page's
  * optional scores_input_fn (Parameters: a loader of the score of a (token,
  * expert) pair), here one of two fixed functions. Saves writing and reading
- * a [T, E] scores tensor. Each score is evaluated in binary64 (softmax: max
- * and sum over the token's experts) and rounded once to binary32; routing
- * then proceeds exactly as in moe_router_group_limited, and expert_weights
- * (dtype = logits_dtype) come from these scores.
+ * a [T, E] scores tensor. Each score is evaluated in binary64 and rounded
+ * once to binary32; routing then proceeds exactly as in
+ * moe_router_group_limited, and expert_weights (dtype = logits_dtype) come
+ * from these scores. The binary64 steps are fixed, so the scores do not
+ * depend on a math library: exp(x) by Cody and Waite's reduction with ln 2
+ * split in two binary64 parts, the Taylor polynomial of exp up to degree 13
+ * by Horner's rule with fused multiply-adds, and 2^k applied as two exact
+ * powers of two (0 below -745.2, +inf above 709.78); the softmax subtracts
+ * the token's largest logit and divides by the pairwise sum of the E
+ * exponentials (a balanced tree over the experts in index order, padded
+ * with zeros to a power of two).
  *
  *   router_logits    in [T, E], dtype logits_dtype.
  *   other arguments, validation and support as moe_router_group_limited;

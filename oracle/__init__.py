@@ -84,6 +84,10 @@ def _load():
             getattr(lib, fn).restype = None
         lib.moe_oracle_num_threads.argtypes = []
         lib.moe_oracle_num_threads.restype = ctypes.c_int
+        lib.moe_oracle_exp.argtypes = [ctypes.c_double]
+        lib.moe_oracle_exp.restype = ctypes.c_double
+        lib.moe_oracle_pairwise_sum.argtypes = [p, i64]
+        lib.moe_oracle_pairwise_sum.restype = ctypes.c_double
         lib.moe_oracle_set_num_threads.argtypes = [ctypes.c_int]
         lib.moe_oracle_set_num_threads.restype = None
         _lib = lib
@@ -194,6 +198,17 @@ def finalize(down, down_dtype: int, restore_order, router_weight, weight_dtype: 
                                      weight_dtype, T, K, H)
     _check(rc, "finalize")
     return out
+
+
+def exp(x: float) -> float:
+    """The score functions' binary64 exponential (one value)."""
+    return float(_load().moe_oracle_exp(float(x)))
+
+
+def pairwise_sum(v) -> float:
+    """The softmax denominator's binary64 pairwise sum of v, in index order."""
+    a = np.ascontiguousarray(v, dtype=np.float64)
+    return float(_load().moe_oracle_pairwise_sum(_ptr(a), a.size))
 
 
 def f32_to_bf16(x) -> np.ndarray:

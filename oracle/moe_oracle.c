@@ -204,26 +204,91 @@ static int keyed_desc(const void* a, const void* b) {
  *     evaluated in binary64, rounded to binary32, then to the output dtype.
  */
 /*
+ * Binary64 exponential of the score functions. Not libm's exp, whose last
+ * bit is the library's own choice, but a fixed published method, so that
+ * any implementation of the same steps produces the same bits:
+ *   - argument reduction of Cody and Waite (Software Manual for the
+ *     Elementary Functions, 1980): k = x / ln2 rounded to the nearest
+ *     integer (ties to even), r = (x - k * LN2_HI) - k * LN2_LO, each
+ *     subtraction one fused multiply-add, with LN2_HI the binary64 value
+ *     nearest ln 2 and LN2_LO the binary64 value nearest ln 2 - LN2_HI;
+ *   - exp(r) by its Taylor series about 0 up to r^13 / 13! (|r| <= ln2 / 2
+ *     leaves a remainder below 2^-56 relative), evaluated by Horner's rule
+ *     from the highest power down, one fused multiply-add per term; the
+ *     coefficient of r^n is 1 / n! rounded once (n! is exact in binary64);
+ *   - scaling by 2^k as two exact powers of two, 2^(k/2) then
+ *     2^(k - k/2) (k/2 truncated towards zero), so only the last product
+ *     rounds (into the subnormal range or to infinity).
+ * Outside [-745.2, 709.78] the result is 0 or +inf; NaN stays NaN.
+ * Within two binary64 ulps of exp(x) (pinned against a correctly rounded
+ * reference).
+ */
+double moe_oracle_exp(double x) {
+    const double LN2_HI = 0x1.62e42fefa39efp-1;
+    const double LN2_LO = 0x1.abc9e3b39803fp-56;
+    const double INV_LN2 = 0x1.71547652b82fep+0;
+    if (x != x) return x;
+    if (x > 709.78) return INFINITY;
+    if (x < -745.2) return 0.0;
+    const double kd = rint(x * INV_LN2);
+    double r = fma(-kd, LN2_HI, x);
+    r = fma(-kd, LN2_LO, r);
+    double fact = 1.0;
+    for (int n = 2; n <= 13; ++n) fact *= (double)n; /* 13!, exact */
+    double p = 1.0 / fact;
+    for (int n = 12; n >= 0; --n) {
+        fact /= (double)(n + 1); /* n!, exact */
+        p = fma(p, r, 1.0 / fact);
+    }
+    const int k = (int)kd;
+    const int k1 = k / 2, k2 = k - k1;
+    return (p * ldexp(1.0, k1)) * ldexp(1.0, k2);
+}
+
+/*
+ * Sum of v[0..n) in binary64 as a balanced pairwise tree in index order:
+ * the values padded with zeros to the next power of two P, then for
+ * w = 1, 2, 4, ... < P every t[i] with i a multiple of 2w becomes
+ * t[i] + t[i + w]; the sum is t[0]. Adding the zero padding is exact, so
+ * the result depends only on v (and equals the same tree over any larger
+ * power of two).
+ */
+double moe_oracle_pairwise_sum(const double* v, int64_t n) {
+    if (n <= 0) return 0.0;
+    int64_t P = 1;
+    while (P < n) P *= 2;
+    double* t = (double*)calloc((size_t)P, sizeof(double));
+    if (!t) return NAN;
+    for (int64_t i = 0; i < n; ++i) t[i] = v[i];
+    for (int64_t w = 1; w < P; w *= 2)
+        for (int64_t i = 0; i < P; i += 2 * w) t[i] = t[i] + t[i + w];
+    const double s = t[0];
+    free(t);
+    return s;
+}
+
+/*
  * Routing scores of one token (router page, Parameters: scores_input_fn, an
  * optional loader of the scores of a (token, expert) pair). score_fn 0
  * loads them from the input; 1 and 2 compute them from the input taken as
  * logits: 1 is the logistic sigmoid 1 / (1 + exp(-x)) of each logit, 2 the
  * softmax over the token's E logits, exp(x_e - max) / sum_j exp(x_j - max).
- * Both are evaluated in binary64 (sum in ascending expert order) and
+ * Both are evaluated in binary64 with moe_oracle_exp (the softmax
+ * denominator as the pairwise sum above, over experts in index order) and
  * rounded once to binary32, the scores' working precision.
  */
-static void token_scores(float* s, const void* in, int32_t dtype, int32_t score_fn, int64_t t,
-                         int32_t E) {
+static void token_scores(float* s, double* ex, const void* in, int32_t dtype, int32_t score_fn,
+                         int64_t t, int32_t E) {
     for (int32_t e = 0; e < E; ++e) s[e] = load_as_f32(in, dtype, t * (int64_t)E + e);
     if (score_fn == OR_SCORE_SIGMOID) {
-        for (int32_t e = 0; e < E; ++e) s[e] = (float)(1.0 / (1.0 + exp(-(double)s[e])));
+        for (int32_t e = 0; e < E; ++e) s[e] = (float)(1.0 / (1.0 + moe_oracle_exp(-(double)s[e])));
     } else if (score_fn == OR_SCORE_SOFTMAX) {
         double m = (double)s[0];
         for (int32_t e = 1; e < E; ++e)
             if ((double)s[e] > m) m = (double)s[e];
-        double sum = 0.0;
-        for (int32_t e = 0; e < E; ++e) sum += exp((double)s[e] - m);
-        for (int32_t e = 0; e < E; ++e) s[e] = (float)(exp((double)s[e] - m) / sum);
+        for (int32_t e = 0; e < E; ++e) ex[e] = moe_oracle_exp((double)s[e] - m);
+        const double sum = moe_oracle_pairwise_sum(ex, E);
+        for (int32_t e = 0; e < E; ++e) s[e] = (float)(ex[e] / sum);
     }
 }
 
@@ -245,19 +310,20 @@ int moe_oracle_router(int32_t* expert_indices, void* expert_weights, const void*
 #pragma omp parallel
     {
         float* s = (float*)malloc(sizeof(float) * (size_t)E);
+        double* ex = (double*)malloc(sizeof(double) * (size_t)E);
         float* b = (float*)malloc(sizeof(float) * (size_t)E);
         keyed_t* grp = (keyed_t*)malloc(sizeof(keyed_t) * (size_t)S);
         keyed_t* gsc = (keyed_t*)malloc(sizeof(keyed_t) * (size_t)n_groups);
         keyed_t* cand = (keyed_t*)malloc(sizeof(keyed_t) * (size_t)E);
         char* kept = (char*)malloc((size_t)n_groups);
-        if (!s || !b || !grp || !gsc || !cand || !kept) {
+        if (!s || !ex || !b || !grp || !gsc || !cand || !kept) {
 #pragma omp atomic write
             rc = OR_NO_MEM;
         } else {
 #pragma omp for schedule(static)
             for (int64_t t = 0; t < T; ++t) {
                 /* 1. scores, biased scores */
-                token_scores(s, scores, scores_dtype, score_fn, t, E);
+                token_scores(s, ex, scores, scores_dtype, score_fn, t, E);
                 for (int32_t e = 0; e < E; ++e) b[e] = s[e] + load_as_f32(bias, bias_dtype, e);
                 /* 2. group scores */
                 for (int32_t g = 0; g < n_groups; ++g) {
@@ -299,6 +365,7 @@ int moe_oracle_router(int32_t* expert_indices, void* expert_weights, const void*
             }
         }
         free(s);
+        free(ex);
         free(b);
         free(grp);
         free(gsc);

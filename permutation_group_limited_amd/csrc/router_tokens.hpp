@@ -168,21 +168,74 @@ constexpr int kScoreLoad = 0;
 constexpr int kScoreSigmoid = 1;
 constexpr int kScoreSoftmax = 2;
 
+// 1 / n! rounded once (n! is exact in binary64 for n <= 18); folded by the
+// compiler, whose constant arithmetic rounds to nearest even.
+constexpr double inv_factorial(int n) {
+  double f = 1.0;
+  for (int i = 2; i <= n; ++i) f *= static_cast<double>(i);
+  return 1.0 / f;
+}
+
+// 2^n for -1022 <= n <= 1023, built from its exponent field.
+__device__ __forceinline__ double pow2_normal(int n) {
+  return __longlong_as_double(static_cast<long long>(n + 1023) << 52);
+}
+
+// Binary64 exponential by a fixed published method, so that its bits do
+// not depend on a math library: Cody and Waite's reduction (Software Manual
+// for the Elementary Functions, 1980) x = k ln2 + r, k = round-to-even of
+// x / ln2, r = (x - k LN2_HI) - k LN2_LO with ln2 split into its nearest
+// binary64 value and the nearest binary64 value of the remainder, each
+// step one fused multiply-add; exp(r) as its Taylor polynomial up to
+// r^13 / 13! by Horner's rule with fused multiply-adds; then 2^k applied as
+// two exact powers of two, 2^(k/2) and 2^(k - k/2), so that only the last
+// product rounds. 0 below -745.2, +inf above 709.78, NaN kept.
+__device__ __forceinline__ double exp_f64(double x) {
+  constexpr double kLn2Hi = 0x1.62e42fefa39efp-1;
+  constexpr double kLn2Lo = 0x1.abc9e3b39803fp-56;
+  constexpr double kInvLn2 = 0x1.71547652b82fep+0;
+  const double xc = __builtin_fmin(__builtin_fmax(x, -745.2), 709.78);
+  const double kd = __builtin_rint(xc * kInvLn2);
+  double r = __builtin_fma(-kd, kLn2Hi, xc);
+  r = __builtin_fma(-kd, kLn2Lo, r);
+  double p = inv_factorial(13);
+#pragma unroll
+  for (int n = 12; n >= 0; --n) p = __builtin_fma(p, r, inv_factorial(n));
+  const int k = static_cast<int>(kd);
+  const int k1 = k / 2;
+  double y = (p * pow2_normal(k1)) * pow2_normal(k - k1);
+  y = x > 709.78 ? __builtin_inf() : y;
+  y = x < -745.2 ? 0.0 : y;
+  return x != x ? x : y;
+}
+
 __device__ __forceinline__ float sigmoid_f64(float x) {
-  return static_cast<float>(1.0 / (1.0 + exp(-static_cast<double>(x))));
+  return static_cast<float>(1.0 / (1.0 + exp_f64(-static_cast<double>(x))));
 }
 
 __device__ __forceinline__ float key_to_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
 }
 
-// Sum of v over the token's LPT lanes (xor butterfly; every lane of the
-// segment ends with the same value because each pairwise add is commutative).
-template <int LPT>
-__device__ __forceinline__ double segment_sum_f64(double v) {
+// Pairwise sum of the token's E' = EPL * LPT values in expert order: a
+// balanced tree inside the lane's EPL consecutive experts, then the xor
+// butterfly over the token's LPT lanes, which continues the same tree (step
+// `off` adds the partial sums of the neighbouring blocks of off lanes; each
+// add is commutative, so every lane of the segment ends with the root).
+template <int EPL, int LPT>
+__device__ __forceinline__ double pairwise_sum_f64(const double (&v)[EPL]) {
+  double t[EPL];
 #pragma unroll
-  for (int off = 1; off < LPT; off <<= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  for (int i = 0; i < EPL; ++i) t[i] = v[i];
+#pragma unroll
+  for (int w = 1; w < EPL; w *= 2) {
+#pragma unroll
+    for (int i = 0; i + w < EPL; i += 2 * w) t[i] = t[i] + t[i + w];
+  }
+  double s = t[0];
+#pragma unroll
+  for (int off = 1; off < LPT; off <<= 1) s += __shfl_xor(s, off, kWave);
+  return s;
 }
 
 // Routes the tokens of workgroup `block` (WPB waves of kWave / LPT tokens
@@ -247,13 +300,11 @@ __device__ __forceinline__ void route_tokens(
 #pragma unroll
     for (int i = 0; i < EPL; ++i) km = present[i] ? umax(km, ordered_key(s[i])) : km;
     sm_max = static_cast<double>(key_to_float(segment_max<LPT>(km)));
-    double ex[EPL], part = 0.0;
+    double ex[EPL];
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      ex[i] = present[i] ? exp(static_cast<double>(s[i]) - sm_max) : 0.0;
-      part += ex[i];
-    }
-    sm_sum = segment_sum_f64<LPT>(part);
+    for (int i = 0; i < EPL; ++i)
+      ex[i] = present[i] ? exp_f64(static_cast<double>(s[i]) - sm_max) : 0.0;
+    sm_sum = pairwise_sum_f64<EPL, LPT>(ex);
 #pragma unroll
     for (int i = 0; i < EPL; ++i) s[i] = static_cast<float>(ex[i] / sm_sum);
   }

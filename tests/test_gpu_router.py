@@ -271,3 +271,31 @@ def test_two_tokens_per_wave_logits(fn, dt):
         assert_weights_equal(gw, ow)
     else:
         assert_weights_equal(bf16_bits(gw), ow)
+
+
+@pytest.mark.parametrize("row", [0, 1])
+@pytest.mark.parametrize("T", [1, 8192])
+def test_softmax_sum_order_rows(row, T):
+    # logits on which another order of the softmax denominator's additions
+    # changes a binary32 score (tests/golden/softmax_sum_order_logits.txt):
+    # the kernel must add in the oracle's pairwise order. No normalisation
+    # and scale 1, so the weights are the scores; the bias makes the flipping
+    # expert one of the K selected. T = 8192 at E = 256 takes the
+    # two-tokens-per-wave form.
+    from test_oracle_scorefn import sum_order_rows
+    E, flip, x1 = sum_order_rows()[row]
+    log("router softmax sum-order row", E, flip, T)
+    x = torch.from_numpy(np.repeat(x1, T, axis=0))
+    if E == 4:
+        K, bias = 4, torch.zeros(E)
+    else:
+        K = 32
+        bias = torch.zeros(E)
+        lo = flip - flip % K
+        bias[lo:lo + K] = 10.0
+    gfn, ofn = FNS["softmax"]
+    gi, gw = gpu_router_logits(x, bias, gfn, K, 1, 1, False, 1.0)
+    oi, ow = oracle.router(x.numpy(), bias.numpy(), K, 1, 1, False, 1.0, score_fn=ofn)
+    assert np.array_equal(gi, oi)
+    assert_weights_equal(gw, ow)
+    assert np.any(gi[0] == flip)

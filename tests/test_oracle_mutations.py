@@ -94,10 +94,22 @@ MUTATIONS = [
      "b[e] = s[e] + load_as_f32(bias, scores_dtype, e);"),
     ("sigmoid of the negated logit", SCOREFN, "exp(-(double)s[e])", "exp((double)s[e])"),
     ("softmax sum misses the last expert", SCOREFN,
-     "for (int32_t e = 0; e < E; ++e) sum += exp((double)s[e] - m);",
-     "for (int32_t e = 0; e + 1 < E; ++e) sum += exp((double)s[e] - m);"),
+     "const double sum = moe_oracle_pairwise_sum(ex, E);",
+     "const double sum = moe_oracle_pairwise_sum(ex, E - 1);"),
     ("softmax evaluated in binary32", SCOREFN,
-     "s[e] = (float)(exp((double)s[e] - m) / sum);", "s[e] = expf(s[e] - (float)m) / (float)sum;"),
+     "s[e] = (float)(ex[e] / sum);", "s[e] = expf(s[e] - (float)m) / (float)sum;"),
+    ("softmax denominator summed left to right", SCOREFN,
+     "const double sum = moe_oracle_pairwise_sum(ex, E);",
+     "double sum = 0.0;\n        for (int32_t e = 0; e < E; ++e) sum += ex[e];"),
+    ("pairwise sum taken left to right", SCOREFN,
+     "for (int64_t w = 1; w < P; w *= 2)\n        for (int64_t i = 0; i < P; i += 2 * w) t[i] = t[i] + t[i + w];",
+     "for (int64_t i = 1; i < P; ++i) t[0] = t[0] + t[i];"),
+    ("exp series one term short", SCOREFN,
+     ["for (int n = 2; n <= 13; ++n)", "for (int n = 12; n >= 0; --n)"],
+     ["for (int n = 2; n <= 12; ++n)", "for (int n = 11; n >= 0; --n)"]),
+    ("exp reduction without the low part of ln 2", SCOREFN, "r = fma(-kd, LN2_LO, r);", ";"),
+    ("exp scaled by 2^(k+1)", SCOREFN, "const int k1 = k / 2, k2 = k - k1;",
+     "const int k1 = k / 2, k2 = k - k1 + 1;"),
 ]
 
 
