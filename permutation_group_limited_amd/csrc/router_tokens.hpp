@@ -140,10 +140,13 @@ __device__ __forceinline__ uint32_t segment_max(uint32_t v) {
   return v;
 }
 
-// Descending bitonic sorting network over EPL (a power of two) distinct
-// 64-bit values, unrolled at compile time.
+// Descending bitonic sorting network over EPL (a power of two) pairs
+// (key, rel), ordered as the distinct 64-bit values key << 32 | rel, and
+// unrolled at compile time. Each compare-exchange is one 64-bit compare and
+// four 32-bit selects (on the packed values the compiler would form a
+// maximum and a minimum, with a compare each).
 template <int EPL>
-__device__ __forceinline__ void sort_desc_u64(uint64_t (&p)[EPL]) {
+__device__ __forceinline__ void sort_desc_pairs(uint32_t (&key)[EPL], uint32_t (&rel)[EPL]) {
 #pragma unroll
   for (int k = 2; k <= EPL; k <<= 1) {
 #pragma unroll
@@ -152,10 +155,14 @@ __device__ __forceinline__ void sort_desc_u64(uint64_t (&p)[EPL]) {
       for (int i = 0; i < EPL; ++i) {
         const int l = i ^ j;
         if (l > i) {
-          const uint64_t a = p[i], b = p[l];
+          const uint64_t a = (static_cast<uint64_t>(key[i]) << 32) | rel[i];
+          const uint64_t b = (static_cast<uint64_t>(key[l]) << 32) | rel[l];
           const bool sw = ((i & k) == 0) ? (a < b) : (a > b);
-          p[i] = sw ? b : a;
-          p[l] = sw ? a : b;
+          const uint32_t ka = key[i], kb = key[l], ra = rel[i], rb = rel[l];
+          key[i] = sw ? kb : ka;
+          key[l] = sw ? ka : kb;
+          rel[i] = sw ? rb : ra;
+          rel[l] = sw ? ra : rb;
         }
       }
     }
@@ -399,24 +406,21 @@ __device__ __forceinline__ void route_tokens(
   // among lanes whose head key equals it the lowest lane wins, which is the
   // lowest expert id because lanes hold ascending, disjoint id ranges. The
   // winner pops its head. Round k yields slot k.
-  uint64_t pk[EPL];
+  uint32_t kv[EPL], rel[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
-    const uint32_t key = (tok_ok && kept[i] && present[i]) ? bk[i] : 0u;
-    pk[i] = (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(EPL - 1 - i);
+    kv[i] = (tok_ok && kept[i] && present[i]) ? bk[i] : 0u;
+    rel[i] = static_cast<uint32_t>(EPL - 1 - i);
   }
-  sort_desc_u64<EPL>(pk);
+  sort_desc_pairs<EPL>(kv, rel);
   // The sorted list as keys plus one word of 4-bit element indices (element
   // of position i in bits 4i..4i+3): a pop shifts the keys by one register
   // and the index word by 4 bits.
   using IdxWord = typename std::conditional<(EPL > 8), uint64_t, uint32_t>::type;
-  uint32_t kv[EPL];
   IdxWord iw = 0;
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    kv[i] = static_cast<uint32_t>(pk[i] >> 32);
-    iw |= static_cast<IdxWord>((EPL - 1) - static_cast<uint32_t>(pk[i] & (EPL - 1))) << (4 * i);
-  }
+  for (int i = 0; i < EPL; ++i)
+    iw |= static_cast<IdxWord>((EPL - 1) - rel[i]) << (4 * i);
 
   uint32_t my_id = 0;
   for (int k = 0; k < K; ++k) {
