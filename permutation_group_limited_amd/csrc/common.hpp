@@ -85,9 +85,10 @@ __device__ __forceinline__ typename D::storage to_storage(float f) {
 }
 
 // Monotone map binary32 -> uint32 for finite inputs: a < b  <=>  key(a) <
-// key(b), and -0 / +0 map to the same key (IEEE equality).
+// key(b), and -0 / +0 map to the same key (IEEE equality): adding +0 turns
+// -0 into +0 and leaves every other value as it is (round to nearest).
 __device__ __forceinline__ uint32_t ordered_key(float v) {
-  const uint32_t u = (v == 0.0f) ? 0u : __float_as_uint(v);
+  const uint32_t u = __float_as_uint(v + 0.0f);
   const uint32_t flip = static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u;
   return u ^ flip;  // negative: all bits flipped; positive: sign bit set
 }

@@ -478,17 +478,29 @@ __device__ __forceinline__ void route_tokens(
 
   // ---- weights from the unbiased scores -----------------------------------
   // Slot `sub`'s score is still in the registers of the lane that holds
-  // its expert: fetch it across lanes (one ds_bpermute per element
-  // register) instead of reading the row again.
+  // its expert. Powers of two with several experts per lane: every lane
+  // stores its scores in this wave's LDS row (the token's scores in expert
+  // order) and each slot reads its own, without reading the input again
+  // (LDS operations of one wave take effect in order). Otherwise one
+  // ds_bpermute per element register.
   const bool slot = tok_ok && sub < K;
   if (my_id >= static_cast<uint32_t>(E)) my_id = 0;  // unreachable with finite scores
-  const int owner = tok_lane0 + static_cast<int>(my_id / EPL);
-  const int elem = static_cast<int>(my_id % EPL);
   float u = 0.0f;
+  if constexpr (!GEN && EPL > 1) {
+    __shared__ float score_row[WPB][EPL * kWave];
+    float* row = score_row[wave];
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const float v = __shfl(s[i], owner, kWave);
-    u = (i == elem) ? v : u;
+    for (int i = 0; i < EPL; ++i) row[lane * EPL + i] = s[i];
+    __builtin_amdgcn_wave_barrier();
+    u = row[tok_lane0 * EPL + my_id];
+  } else {
+    const int owner = tok_lane0 + static_cast<int>(my_id / EPL);
+    const int elem = static_cast<int>(my_id % EPL);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const float v = __shfl(s[i], owner, kWave);
+      u = (i == elem) ? v : u;
+    }
   }
   // Normalise and scale in binary64, rounded once to binary32: the sum of
   // the K selected scores in slot order (each widened exactly), a correctly
