@@ -433,46 +433,64 @@ __device__ __forceinline__ void route_tokens(
   for (int i = 0; i < EPL; ++i)
     iw |= static_cast<IdxWord>((EPL - 1) - rel[i]) << (4 * i);
 
+  // LDS scratch of each wave (power-of-two layouts with several experts per
+  // lane): its sorted lists during the top-K of two tokens per wave, then
+  // its scores for the weights. One word where unused.
+  constexpr int kScratchWords = (!GEN && EPL > 1) ? (EPL + 1) * kWave : 1;
+  __shared__ __align__(16) uint32_t wave_lds[WPB][kScratchWords];
   uint32_t my_id = 0;
-  for (int k = 0; k < K; ++k) {
-    const uint32_t head = kv[0];
-    const uint64_t top = __ballot(head == segment_max<LPT>(head));
-    bool pop;
-    if constexpr (LPT == kWave) {
-      // the winner and its element are wave-uniform; slot k goes to lane k
-      const int win = __builtin_ctzll(static_cast<unsigned long long>(top));
-      const uint32_t elem =
-          static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(iw & 0xFu), win));
-      my_id = write_lane(static_cast<uint32_t>(win * EPL) + elem, k, my_id);
-      pop = lane == win;
-    } else if constexpr (LPT == kWave / 2 && EPL > 1) {
-      // two tokens per wave (K <= 32, checked by the host): each half's
-      // winner is the lowest set bit of its half of the ballot (every half
-      // has one: its maximum is one of its heads), so both winners, their
-      // elements and the two slot ids are wave-uniform; slot k of the
-      // tokens goes to lanes k and 32 + k
+  if constexpr (LPT == kWave / 2 && EPL > 1) {
+    // Two tokens per wave (K <= 32, checked by the host): each half's
+    // winner is the lowest set bit of its half of the ballot (every half
+    // has one: its maximum is one of its heads), so both winners, their
+    // elements and the two slot ids are wave-uniform; slot k of the tokens
+    // goes to lanes k and 32 + k. The sorted lists sit in this wave's LDS
+    // scratch, position p of lane l at word p * 64 + l (position EPL holds
+    // the empty key): a pop advances the lane's position and reads its next
+    // head, instead of shifting EPL registers.
+#pragma unroll
+    for (int p = 0; p < EPL; ++p) wave_lds[wave][p * kWave + lane] = kv[p];
+    wave_lds[wave][EPL * kWave + lane] = 0u;
+    __builtin_amdgcn_wave_barrier();
+    uint32_t pos = 0u;
+    for (int k = 0; k < K; ++k) {
+      const uint32_t head = wave_lds[wave][pos * kWave + lane];
+      const uint64_t top = __ballot(head == segment_max<LPT>(head));
       const int w_lo = __builtin_ctz(static_cast<uint32_t>(top));
       const int w_hi = 32 + __builtin_ctz(static_cast<uint32_t>(top >> 32));
-      const int e4 = static_cast<int>(iw & 0xFu);
+      const int e4 = static_cast<int>((iw >> (4u * pos)) & 0xFu);
       const uint32_t el_lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(e4, w_lo));
       const uint32_t el_hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(e4, w_hi));
-      const uint32_t id_lo = static_cast<uint32_t>(w_lo * EPL) + el_lo;
-      const uint32_t id_hi = static_cast<uint32_t>((w_hi - 32) * EPL) + el_hi;
-      my_id = write_lane(id_lo, k, my_id);
-      my_id = write_lane(id_hi, 32 + k, my_id);
-      pop = lane == w_lo || lane == w_hi;
-    } else {
-      // one expert per lane, several tokens per wave
-      static_assert(EPL == 1, "several tokens per wave need one expert per lane or two tokens");
-      const int win = __builtin_ctzll(static_cast<unsigned long long>(top & segmask));
-      if (sub == k) my_id = static_cast<uint32_t>(win - tok_lane0);
-      pop = lane == win;
+      my_id = write_lane(static_cast<uint32_t>(w_lo * EPL) + el_lo, k, my_id);
+      my_id = write_lane(static_cast<uint32_t>((w_hi - 32) * EPL) + el_hi, 32 + k, my_id);
+      pos += (lane == w_lo || lane == w_hi) ? 1u : 0u;
     }
-    if (pop) {
+    __builtin_amdgcn_wave_barrier();  // the scratch is rewritten with the scores below
+  } else {
+    for (int k = 0; k < K; ++k) {
+      const uint32_t head = kv[0];
+      const uint64_t top = __ballot(head == segment_max<LPT>(head));
+      bool pop;
+      if constexpr (LPT == kWave) {
+        // the winner and its element are wave-uniform; slot k goes to lane k
+        const int win = __builtin_ctzll(static_cast<unsigned long long>(top));
+        const uint32_t elem =
+            static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(iw & 0xFu), win));
+        my_id = write_lane(static_cast<uint32_t>(win * EPL) + elem, k, my_id);
+        pop = lane == win;
+      } else {
+        // one expert per lane, several tokens per wave
+        static_assert(EPL == 1, "several tokens per wave need one expert per lane or two tokens");
+        const int win = __builtin_ctzll(static_cast<unsigned long long>(top & segmask));
+        if (sub == k) my_id = static_cast<uint32_t>(win - tok_lane0);
+        pop = lane == win;
+      }
+      if (pop) {
 #pragma unroll
-      for (int i = 0; i + 1 < EPL; ++i) kv[i] = kv[i + 1];
-      kv[EPL - 1] = 0u;
-      iw >>= 4;
+        for (int i = 0; i + 1 < EPL; ++i) kv[i] = kv[i + 1];
+        kv[EPL - 1] = 0u;
+        iw >>= 4;
+      }
     }
   }
 
@@ -487,12 +505,10 @@ __device__ __forceinline__ void route_tokens(
   if (my_id >= static_cast<uint32_t>(E)) my_id = 0;  // unreachable with finite scores
   float u = 0.0f;
   if constexpr (!GEN && EPL > 1) {
-    __shared__ float score_row[WPB][EPL * kWave];
-    float* row = score_row[wave];
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) row[lane * EPL + i] = s[i];
+    for (int i = 0; i < EPL; ++i) wave_lds[wave][lane * EPL + i] = __float_as_uint(s[i]);
     __builtin_amdgcn_wave_barrier();
-    u = row[tok_lane0 * EPL + my_id];
+    u = __uint_as_float(wave_lds[wave][tok_lane0 * EPL + my_id]);
   } else {
     const int owner = tok_lane0 + static_cast<int>(my_id / EPL);
     const int elem = static_cast<int>(my_id % EPL);
