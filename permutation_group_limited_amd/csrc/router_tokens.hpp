@@ -463,7 +463,8 @@ __device__ __forceinline__ void route_tokens(
       const uint32_t el_hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(e4, w_hi));
       my_id = write_lane(static_cast<uint32_t>(w_lo * EPL) + el_lo, k, my_id);
       my_id = write_lane(static_cast<uint32_t>((w_hi - 32) * EPL) + el_hi, 32 + k, my_id);
-      pos += (lane == w_lo || lane == w_hi) ? 1u : 0u;
+      // the two winners advance (a uniform lane mask, no per-lane compares)
+      pos += __builtin_amdgcn_inverse_ballot_w64((1ull << w_lo) | (1ull << w_hi)) ? 1u : 0u;
     }
     __builtin_amdgcn_wave_barrier();  // the scratch is rewritten with the scores below
   } else {
