@@ -436,7 +436,12 @@ __device__ __forceinline__ void route_tokens(
   // LDS scratch of each wave (power-of-two layouts with several experts per
   // lane): its sorted lists during the top-K of two tokens per wave, then
   // its scores for the weights. One word where unused.
-  constexpr int kScratchWords = (!GEN && EPL > 1) ? (EPL + 1) * kWave : 1;
+  // Scores are stored with a lane stride of EPL + 4 words from 8 experts a
+  // lane up: the 16-byte stores of 8 consecutive lanes then cover all 32
+  // banks once (a stride of EPL words would put two lanes on each bank).
+  constexpr int kScoreStride = EPL >= 8 ? EPL + 4 : EPL;
+  constexpr int kScratchWords =
+      (!GEN && EPL > 1) ? ((EPL + 1) > kScoreStride ? EPL + 1 : kScoreStride) * kWave : 1;
   __shared__ __align__(16) uint32_t wave_lds[WPB][kScratchWords];
   uint32_t my_id = 0;
   if constexpr (LPT == kWave / 2 && EPL > 1) {
@@ -498,8 +503,8 @@ __device__ __forceinline__ void route_tokens(
   // ---- weights from the unbiased scores -----------------------------------
   // Slot `sub`'s score is still in the registers of the lane that holds
   // its expert. Powers of two with several experts per lane: every lane
-  // stores its scores in this wave's LDS row (the token's scores in expert
-  // order) and each slot reads its own, without reading the input again
+  // stores its scores in this wave's LDS scratch and each slot reads its
+  // own, without reading the input again
   // (LDS operations of one wave take effect in order). Otherwise one
   // ds_bpermute per element register.
   const bool slot = tok_ok && sub < K;
@@ -507,9 +512,10 @@ __device__ __forceinline__ void route_tokens(
   float u = 0.0f;
   if constexpr (!GEN && EPL > 1) {
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) wave_lds[wave][lane * EPL + i] = __float_as_uint(s[i]);
+    for (int i = 0; i < EPL; ++i) wave_lds[wave][lane * kScoreStride + i] = __float_as_uint(s[i]);
     __builtin_amdgcn_wave_barrier();
-    u = __uint_as_float(wave_lds[wave][tok_lane0 * EPL + my_id]);
+    u = __uint_as_float(
+        wave_lds[wave][(tok_lane0 + static_cast<int>(my_id) / EPL) * kScoreStride + my_id % EPL]);
   } else {
     const int owner = tok_lane0 + static_cast<int>(my_id / EPL);
     const int elem = static_cast<int>(my_id % EPL);
