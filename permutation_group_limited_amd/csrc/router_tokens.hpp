@@ -457,13 +457,18 @@ __device__ __forceinline__ void route_tokens(
     for (int p = 0; p < EPL; ++p) wave_lds[wave][p * kWave + lane] = kv[p];
     wave_lds[wave][EPL * kWave + lane] = 0u;
     __builtin_amdgcn_wave_barrier();
+    static_assert(EPL <= 8, "two tokens per wave take E <= 256: 4-bit indices in one word");
     uint32_t pos = 0u;
     for (int k = 0; k < K; ++k) {
-      const uint32_t head = wave_lds[wave][pos * kWave + lane];
+      // A lane is popped at most EPL times while its token has candidates
+      // left; a half without a valid token (the ragged end of the batch)
+      // keeps popping its lowest lane, which stays on the empty row.
+      const uint32_t at = pos < static_cast<uint32_t>(EPL) ? pos : static_cast<uint32_t>(EPL);
+      const uint32_t head = wave_lds[wave][at * kWave + lane];
       const uint64_t top = __ballot(head == segment_max<LPT>(head));
       const int w_lo = __builtin_ctz(static_cast<uint32_t>(top));
       const int w_hi = 32 + __builtin_ctz(static_cast<uint32_t>(top >> 32));
-      const int e4 = static_cast<int>((iw >> (4u * pos)) & 0xFu);
+      const int e4 = static_cast<int>(__builtin_amdgcn_ubfe(iw, 4u * at, 4u));  // past EPL: unused
       const uint32_t el_lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(e4, w_lo));
       const uint32_t el_hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(e4, w_hi));
       my_id = write_lane(static_cast<uint32_t>(w_lo * EPL) + el_lo, k, my_id);
