@@ -20,12 +20,16 @@
 //    ds_swizzle and, for 64-lane groups, ds_bpermute; groups are ranked by
 //    counting the groups that beat each one (ties: lower group index).
 //  * top-K: each lane sorts its EPL (key, expert) pairs (key = biased score
-//    mapped to an order-preserving uint32); then K rounds of: segment max of
-//    the lane heads (DPP max steps and v_readlane), a ballot of the lanes
-//    whose head equals it, the lowest such lane wins (lowest expert id: the
-//    lower-index tie rule) and pops its head. Round k fills slot k, so the
-//    slots come out in (score desc, id asc) order.
-//  * weights: the K winners' unbiased scores, summed in slot order.
+//    mapped to an order-preserving uint32) with Batcher's odd-even merge
+//    sort; then K rounds of: segment max of the lane heads (DPP max steps
+//    and v_readlane), a ballot of the lanes whose head equals it, the lowest
+//    such lane wins (lowest expert id: the lower-index tie rule) and pops its
+//    head (two tokens per wave: the sorted lists sit in LDS and a pop
+//    advances a position). Round k fills slot k, so the slots come out in
+//    (score desc, id asc) order.
+//  * weights: the K winners' unbiased scores (read back from LDS or the
+//    owner lane's registers), normalised in binary64 with the sum taken in
+//    slot order, times the scaling factor, rounded once.
 #include "router_tokens.hpp"
 
 namespace moe {

@@ -426,7 +426,7 @@ __device__ __forceinline__ void route_tokens(
   sort_desc_pairs<EPL>(kv, rel);
   // The sorted list as keys plus one word of 4-bit element indices (element
   // of position i in bits 4i..4i+3): a pop shifts the keys by one register
-  // and the index word by 4 bits.
+  // and the index word by 4 bits (two tokens per wave: see below).
   using IdxWord = typename std::conditional<(EPL > 8), uint64_t, uint32_t>::type;
   IdxWord iw = 0;
 #pragma unroll
