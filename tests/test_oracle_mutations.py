@@ -6,7 +6,7 @@ kind in the oracle could hide."""
 import os
 import subprocess
 import sys
-import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 import pytest
 
@@ -113,20 +113,53 @@ MUTATIONS = [
 ]
 
 
-@pytest.mark.parametrize("name,tests,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
-def test_pins_catch_planted_mistake(name, tests, old, new, tmp_path):
+def _run_mutant(mutation, workdir):
+    """Build the oracle with one planted mistake and run the pins of its
+    stage against that build (in a child process). Returns (returncode,
+    tail of its output)."""
+    name, tests, old, new = mutation
     src = open(SRC).read()
     olds, news = (old, new) if isinstance(old, list) else ([old], [new])
     for o, n in zip(olds, news):
-        assert src.count(o) >= 1, "mutation no longer applies: " + name
+        if src.count(o) < 1:
+            return None, "mutation no longer applies: " + name
         src = src.replace(o, n)
-    mutated = tmp_path / "moe_oracle_mutant.c"
-    mutated.write_text(src)
-    lib = tmp_path / "libmoe_oracle_mutant.so"
+    d = os.path.join(workdir, "m%d" % MUTATIONS.index(mutation))
+    os.makedirs(d, exist_ok=True)
+    mutated = os.path.join(d, "moe_oracle_mutant.c")
+    with open(mutated, "w") as f:
+        f.write(src)
+    lib = os.path.join(d, "libmoe_oracle_mutant.so")
     subprocess.run(["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
-                    "-o", str(lib), str(mutated), "-lm"], check=True, capture_output=True)
-    env = dict(os.environ, MOE_ORACLE_LIB=str(lib))
+                    "-o", lib, mutated, "-lm"], check=True, capture_output=True)
+    # one OpenMP thread per child: several children run side by side
+    env = dict(os.environ, MOE_ORACLE_LIB=lib, OMP_NUM_THREADS="1")
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
                         "-m", "not gpu", tests], cwd=ROOT, env=env, capture_output=True, text=True,
                        timeout=600)
-    assert r.returncode != 0, "pins did not catch: %s\n%s" % (name, r.stdout[-2000:])
+    return r.returncode, r.stdout[-2000:]
+
+
+@pytest.fixture(scope="module")
+def mutant_results(tmp_path_factory):
+    """Results of every mutant, computed once, a few children at a time
+    (each child is dominated by its interpreter start-up). Under pytest-xdist
+    each case runs its own mutant instead."""
+    if os.environ.get("PYTEST_XDIST_WORKER"):
+        return None
+    workdir = str(tmp_path_factory.mktemp("mutants"))
+    workers = max(1, min(4, (os.cpu_count() or 1) // 2))
+    with ThreadPoolExecutor(workers) as ex:
+        results = list(ex.map(lambda m: _run_mutant(m, workdir), MUTATIONS))
+    return {m[0]: r for m, r in zip(MUTATIONS, results)}
+
+
+@pytest.mark.parametrize("mutation", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_planted_mistake(mutation, mutant_results, tmp_path):
+    name = mutation[0]
+    if mutant_results is None:
+        rc, out = _run_mutant(mutation, str(tmp_path))
+    else:
+        rc, out = mutant_results[name]
+    assert rc is not None, out
+    assert rc != 0, "pins did not catch: %s\n%s" % (name, out)
