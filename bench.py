@@ -397,8 +397,8 @@ def config_report(wk, parity=True):
 
 def oracle_parity(P, out):
     """The step's outputs against the CPU oracle on the same inputs: router
-    indices and weights, every index output bit-exact; finalize within 1 ulp
-    (16-bit output) or 1e-5 of the term magnitude (fp32)."""
+    indices and weights, every index output and the finalize output
+    bit-exact (the largest difference is reported beside it)."""
     import numpy as np
     import torch
 
@@ -433,15 +433,17 @@ def oracle_parity(P, out):
         orde = np.where(o & 0x8000, -(o.astype(np.int64) & 0x7FFF), o & 0x7FFF)
         ulp = np.abs(ordg - orde)
         res["finalize_max_ulp"] = int(ulp.max(initial=0))
-        res["finalize"] = bool(ulp.max(initial=0) <= 1)
+        res["finalize"] = bool(np.array_equal(gb, o))
     else:
         o = oracle.finalize(d, dcode, ind["restore_token_order"], ow, oracle.F32, oracle.F32)
         rows = d[ind["restore_token_order"].astype(np.int64)].astype(np.float64)
         mag = (np.abs(ow.astype(np.float64))[:, :, None] *
                np.abs(rows.reshape(T, K, -1))).sum(1)
-        err = np.abs(out.cpu().numpy().astype(np.float64) - o.astype(np.float64))
+        g = out.cpu().numpy()
+        err = np.abs(g.astype(np.float64) - o.astype(np.float64))
         res["finalize_max_abs_err"] = float(err.max(initial=0.0))
-        res["finalize"] = bool(np.all(err <= 1e-5 * mag))
+        res["finalize_within_1e-5_of_terms"] = bool(np.all(err <= 1e-5 * mag))
+        res["finalize"] = bool(np.array_equal(g.view(np.uint32), o.view(np.uint32)))
     return res
 
 

@@ -60,7 +60,13 @@ struct DF16 {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b)));
   }
   __device__ static __forceinline__ float widen_hi(uint32_t w) { return widen_bits(w >> 16); }
+  // f must stay a rounded binary32 value: left alone, the compiler folds a
+  // binary32 fma feeding this conversion into one mixed-precision fma
+  // (v_fma_mix) that rounds the exact result to binary16 once, which at a
+  // binary16 tie of the binary32 result differs from rounding twice. The
+  // empty asm makes f opaque and costs no instruction.
   __device__ static __forceinline__ uint32_t narrow_bits(float f) {
+    asm("" : "+v"(f));
     return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(f)));
   }
 };

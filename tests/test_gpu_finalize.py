@@ -1,6 +1,7 @@
 """GPU parity: moe_finalize vs the CPU oracle (moe_finalize page:
-description, Args). fp32 output within 1e-5 of the term magnitude, bf16
-output within 1 ulp. Marked gpu."""
+description, Args), bit for bit for every dtype combination: both run one
+fmaf per k in ascending k from +0 in fp32 and round once to the output
+type. Marked gpu."""
 import numpy as np
 import pytest
 import torch
@@ -9,7 +10,7 @@ import oracle
 from permutation_group_limited_amd import binding
 from permutation_group_limited_amd import workloads as wl
 
-from _gpu import (DEV, assert_finalize_close, assert_finalize_matches_in_blocks, bf16_bits,
+from _gpu import (DEV, assert_finalize_equal, assert_finalize_matches_in_blocks, bf16_bits,
                   gpu_finalize, log, oracle_finalize_from, term_magnitude)
 
 pytestmark = pytest.mark.gpu
@@ -38,7 +39,7 @@ def test_random_shapes(ddt, wdt, odt, T, K, H):
     down, w, restore = _inputs(T, K, H, DT[ddt], DT[wdt], seed=T * 100 + K * 10 + H)
     got = gpu_finalize(down.to(DEV), restore, w, DT[odt])
     exp = oracle_finalize_from(down, restore, w, DT[odt])
-    assert_finalize_close(got, exp, term_magnitude(down, restore, w))
+    assert_finalize_equal(got, exp, term_magnitude(down, restore, w))
 
 
 def test_cancellation_is_judged_against_term_magnitude():
@@ -65,7 +66,7 @@ def test_workload_full_size(name):
     down_h = down.cpu()
     exp = oracle_finalize_from(down_h, restore, w, wk.out_dtype)
     mag = term_magnitude(down_h, restore, w) if wk.out_dtype == torch.float32 else None
-    assert_finalize_close(got, exp, mag)
+    assert_finalize_equal(got, exp, mag)
 
 
 def test_skewed_full_size():
@@ -120,7 +121,7 @@ def test_more_than_2_32_work_items():
     sub_down = down[rows].cpu()
     exp = oracle_finalize_from(sub_down, np.arange(rows.numel(), dtype=np.uint32),
                                w[ts].cpu(), torch.bfloat16)
-    assert_finalize_close(out[ts], exp, None)
+    assert_finalize_equal(out[ts], exp, None)
     del down, out, restore
     torch.cuda.empty_cache()
 
@@ -146,3 +147,53 @@ def test_overflow_to_infinity(odt):
         assert np.array_equal(g_np.numpy().view(np.uint32), np.asarray(exp).view(np.uint32))
     else:
         assert np.array_equal(bf16_bits(got), np.asarray(exp, np.uint16))
+
+
+# ---- large shapes ----------------------------------------------------------
+# Millions of outputs per case, so the fp32 sums include thousands that sit
+# exactly halfway between two binary16 (or bf16) values: rounding them once
+# more, to the output type, must follow the fp32 rounding, as in the oracle
+# (a mixed-precision fma rounding the exact sum straight to binary16 would
+# differ there). Ragged H (7160: the last 16-byte column of a 512-element
+# chunk missing), long rows (14336, 16384), every K up to 8, all 16-bit
+# dtype combinations.
+LARGE_CASES = [
+    # T, K, H, down, weight, out
+    (8200, 8, 7168, "bf16", "f32", "bf16"),
+    (4101, 3, 7160, "f16", "f16", "bf16"),
+    (2051, 5, 14336, "bf16", "f32", "f16"),
+    (2053, 1, 16384, "f16", "bf16", "f16"),
+    (4113, 4, 7168, "f16", "f32", "f16"),
+    (8197, 6, 4096, "bf16", "f16", "bf16"),
+    (4099, 7, 8192, "bf16", "f32", "f16"),
+    (8195, 2, 4096, "f16", "bf16", "bf16"),
+]
+
+
+@pytest.mark.parametrize("T,K,H,ddt,wdt,odt", LARGE_CASES,
+                         ids=["T%d-K%d-H%d-%s-%s-%s" % c for c in LARGE_CASES])
+def test_large_shapes_equal_oracle(T, K, H, ddt, wdt, odt):
+    log("finalize large shape", T, K, H, ddt, wdt, odt)
+    down, w, restore = _inputs(T, K, H, DT[ddt], DT[wdt], seed=T + K + H)
+    got = gpu_finalize(down.to(DEV), restore, w, DT[odt])
+    exp = oracle_finalize_from(down, restore, w, DT[odt])
+    assert_finalize_equal(got, exp)
+
+
+@pytest.mark.parametrize("T,K,H", [(4100, 8, 4096), (64, 2, 4104)])
+def test_out_of_range_restore_entries_stay_in_bounds(T, K, H):
+    """Precondition violated on purpose (restore entries >= T*K): the call
+    completes, no access leaves `down` (such an entry reads row 0 with
+    weight 0), and every token whose entries are all in range is exact."""
+    log("finalize out-of-range restore", T, K, H)
+    down, w, restore = _inputs(T, K, H, torch.bfloat16, torch.float32, seed=5)
+    bad_slots = np.array([1, 7, 2 * K + 1, T * K - 1])
+    restore = restore.copy()
+    restore[bad_slots] = np.array([T * K, 0xFFFFFFFF, T * K + 12345, 0x80000000],
+                                  dtype=np.uint32)
+    got = gpu_finalize(down.to(DEV), restore, w, torch.bfloat16)
+    good = np.ones(T, dtype=bool)
+    good[bad_slots // K] = False
+    ok_rest = np.where(restore < T * K, restore, 0).astype(np.uint32)
+    exp = oracle_finalize_from(down, ok_rest, w, torch.bfloat16)
+    assert_finalize_equal(got[torch.from_numpy(good).to(DEV)], np.asarray(exp)[good])
