@@ -22,9 +22,11 @@
  * HIP graph.
  *
  * Errors. Each call returns moe_status_t. Arguments are validated on the
- * host before anything is enqueued; on any error nothing is launched and no
- * output is written. MOE_ERR_HIP means a launch was rejected by the HIP
- * runtime (moe_last_hip_error() gives the hipError_t value). Conditions on
+ * host before anything is enqueued; on a validation error nothing is
+ * launched and no output is written. MOE_ERR_HIP means a launch was
+ * rejected by the HIP runtime (moe_last_hip_error() gives the hipError_t
+ * value); launches of the same call enqueued before it may have run (for
+ * moe_route_and_index, see its workspace note). Conditions on
  * the *contents* of device buffers (expert ids in range, restore_order a
  * permutation, finite scores) are preconditions, not checked: the kernels
  * stay inside every buffer when they are violated, but the values written

@@ -1,7 +1,7 @@
 """GPU parity of the chained path router -> create_indices -> finalize, all
-on the GPU from the same inputs, against the chained oracle: indices and
-weights bit-exact, every finalize output row within 1 bf16 ulp (1e-5 of the
-term magnitude for fp32). Marked gpu."""
+on the GPU from the same inputs, against the chained oracle: indices,
+weights and every finalize output element bit-exact. Also the chain
+captured in a HIP graph and replayed. Marked gpu."""
 import numpy as np
 import pytest
 import torch
@@ -64,3 +64,58 @@ def test_pipeline(name):
     log("pipeline %s: largest finalize difference %s" % (name, worst))
     del down, out
     torch.cuda.empty_cache()
+
+
+def _chain_buffers(wk):
+    T, E, K = wk.T, wk.E, wk.K
+    i32 = lambda *shape: torch.empty(shape, dtype=torch.int32, device=DEV)  # noqa: E731
+    return {"idx": i32(T, K), "w": torch.empty(T, K, dtype=torch.float32, device=DEV),
+            "order": i32(T * K), "restore": i32(T * K), "starts": i32(E + 1), "eids": i32(E),
+            "stats": i32(2), "out": torch.empty(T, wk.H, dtype=wk.out_dtype, device=DEV)}
+
+
+def _run_chain(wk, bufs, s, b, ws, down):
+    binding.moe_router_group_limited(bufs["idx"], bufs["w"], s, b, wk.n_groups, wk.topk_group,
+                                     wk.norm_weights, wk.scale)
+    binding.moe_create_indices(bufs["order"], bufs["starts"], bufs["restore"], bufs["eids"],
+                               bufs["stats"], bufs["idx"], ws)
+    binding.moe_finalize(bufs["out"], down, bufs["restore"], bufs["w"])
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "dsv3"])
+def test_graph_replay_of_the_chain(name):
+    """router -> create_indices -> finalize through the separate entry
+    points, captured once in a HIP graph and replayed four times with eager
+    work in between (every output refilled with a poison value first):
+    each replay equals the eager chain bit for bit."""
+    wk = wl.WORKLOADS[name]
+    log("chain graph replay", wk.describe())
+    down = wl.make_down(wk, device=DEV)
+    s = wl.make_scores(wk).to(DEV)
+    b = wl.make_bias(wk).to(DEV)
+    ws = torch.empty(max(binding.moe_create_indices_workspace_size(wk.T * wk.K, wk.E), 4) // 4,
+                     dtype=torch.int32, device=DEV)
+    eager = _chain_buffers(wk)
+    _run_chain(wk, eager, s, b, ws, down)
+    torch.cuda.synchronize()
+    bufs = _chain_buffers(wk)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        _run_chain(wk, bufs, s, b, ws, down)  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _run_chain(wk, bufs, s, b, ws, down)
+    for rep in range(4):
+        for key, t in bufs.items():
+            t.fill_(float("nan")) if t.is_floating_point() else t.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for key, t in bufs.items():
+            e = eager[key]
+            same = torch.equal(t.view(torch.int16), e.view(torch.int16)) if t.element_size() == 2 \
+                else torch.equal(t.view(torch.int32), e.view(torch.int32))
+            assert same, "replay %d: %s differs from the eager chain" % (rep, key)
