@@ -301,6 +301,7 @@ def main():
             "note": "the same output buffer rewritten call after call: its rows stay in the "
                     "memory-side cache, so part of the write cost never reaches HBM"}
         ex["probes"] = probes(P, args.steps)
+        ex["launch_probes"] = launch_probes()
         ex["router_on_logits"] = router_on_logits(P, args.steps)
         ex["two_batches_in_flight"] = two_batches_in_flight(P, args.steps)
         del P
@@ -489,6 +490,39 @@ def probes(P, steps):
     res["read_phase_plus_write_phase_frac"] = \
         P.bytes["finalize"] / (bound_us * 1e-6) / 1e9 / PEAK_HBM_GBPS
     del big
+    return res
+
+
+def launch_probes():
+    """Fixed costs that bound the small batches, each as GPU time per call
+    with 20 calls per HIP graph (libmoe_probe.so): a launch of one workgroup
+    that does nothing, the same with 1,024 workgroups, one workgroup reading
+    64 KiB, and that read right after a kernel (1,024 waves of 16-byte
+    stores) wrote the 64 KiB. The last minus the write alone is what one
+    launch costs when it reads what the launch before it wrote, as the
+    index step reads the router's counts."""
+    import torch
+
+    from permutation_group_limited_amd import probe
+
+    buf = torch.zeros(1 << 14, dtype=torch.int32, device="cuda:0")  # 64 KiB
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda:0")
+
+    def pair():
+        probe.write(buf)
+        probe.consume(buf, sink)
+
+    cases = {"empty_1_workgroup": lambda: probe.empty(1),
+             "empty_1024_workgroups": lambda: probe.empty(1024),
+             "write_64KiB": lambda: probe.write(buf),
+             "read_64KiB_one_workgroup": lambda: probe.consume(buf, sink),
+             "write_then_read_64KiB": pair}
+    res = {}
+    for name, f in cases.items():
+        f()
+        torch.cuda.synchronize()
+        res[name + "_us"] = graph_replay_us(f)
+    res["read_after_write_us"] = res["write_then_read_64KiB_us"] - res["write_64KiB_us"]
     return res
 
 

@@ -5,7 +5,10 @@
  * that the achievable HBM rates the finalize kernel is judged against are
  * measured in the same run, on the same access patterns: streaming reads
  * with the loads finalize uses, streaming writes with its stores, and its
- * gather without the stores. They are not part of the routing path and
+ * gather without the stores. Two more give the fixed costs that bound the
+ * small batches: a launch that does nothing, and one workgroup reading a
+ * small buffer (after a kernel that wrote it, the latency of handing data
+ * from one launch to the next). They are not part of the routing path and
  * compute nothing of the method.
  *
  * Conventions as in moe_route.h: device pointers owned by the caller,
@@ -57,6 +60,25 @@ moe_status_t moe_probe_write(void* dst, size_t bytes, uint32_t value, void* stre
  */
 moe_status_t moe_probe_gather(const void* rows, const uint32_t* restore, int64_t T, int32_t K,
                               int64_t row_bytes, uint32_t* sink, void* stream);
+
+/*
+ * moe_probe_empty
+ * Launches `workgroups` workgroups of 256 threads that do nothing: the cost
+ * of a launch itself.
+ * Validation: 1 <= workgroups <= 65535.
+ */
+moe_status_t moe_probe_empty(int32_t workgroups, void* stream);
+
+/*
+ * moe_probe_consume
+ * One workgroup of 1024 threads reads `bytes` bytes of `src` (each thread
+ * issues all of its 16-byte loads, up to 16, before using any) and folds
+ * them with XOR; nothing is written unless a fixed pattern appears (one
+ * word to sink[0]).
+ * Validation: bytes a multiple of 16 KiB and at most 256 KiB; src 16-byte
+ * aligned; src and sink non-NULL when bytes > 0.
+ */
+moe_status_t moe_probe_consume(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -2,8 +2,9 @@
 // streaming writes and the finalize gather without its stores, each with the
 // exact load / store instructions and per-wave shapes of finalize_kernel, so
 // that the benchmark can set the finalize kernel's time beside what the
-// memory system delivers to those patterns alone. Not part of the routing
-// path.
+// memory system delivers to those patterns alone; and the fixed costs of
+// small batches: an empty launch, and one workgroup reading a small buffer.
+// Not part of the routing path.
 #include "common.hpp"
 #include "moe_probe.h"
 
@@ -81,6 +82,24 @@ __global__ __launch_bounds__(kBlock) void probe_gather_kernel(
   if (x == kMagic) sink[0] = x;
 }
 
+__global__ __launch_bounds__(kBlock) void probe_empty_kernel() {}
+
+// One workgroup of kConsumeThreads threads; thread i reads vectors i,
+// i + kConsumeThreads, ... (all loads issued before any is used).
+constexpr int kConsumeThreads = 1024;
+constexpr int kConsumeMaxVecs = 16;  // per thread: 256 KiB per call at most
+__global__ __launch_bounds__(kConsumeThreads) void probe_consume_kernel(
+    const u32x4* __restrict__ src, int vecs_per_thread, uint32_t* __restrict__ sink) {
+  u32x4 v[kConsumeMaxVecs];
+#pragma unroll
+  for (int j = 0; j < kConsumeMaxVecs; ++j)
+    v[j] = j < vecs_per_thread ? src[threadIdx.x + j * kConsumeThreads] : u32x4{0u, 0u, 0u, 0u};
+  uint32_t x = 0;
+#pragma unroll
+  for (int j = 0; j < kConsumeMaxVecs; ++j) x ^= fold(v[j]);
+  if (x == kMagic) sink[0] = x;
+}
+
 constexpr size_t kMaxProbeBytes = static_cast<size_t>(1) << 40;
 
 moe_status_t launched() {
@@ -139,6 +158,25 @@ moe_status_t moe_probe_gather(const void* rows, const uint32_t* restore, int64_t
                      static_cast<hipStream_t>(stream), static_cast<const u32x4*>(rows), restore,
                      T, K, row_vecs, static_cast<uint32_t>(cpr), static_cast<uint32_t>(T * K),
                      sink);
+  return launched();
+}
+
+moe_status_t moe_probe_empty(int32_t workgroups, void* stream) {
+  if (workgroups < 1 || workgroups > 65535) return MOE_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(probe_empty_kernel, dim3(static_cast<uint32_t>(workgroups)), dim3(kBlock), 0,
+                     static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+moe_status_t moe_probe_consume(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  constexpr size_t kStep = static_cast<size_t>(kConsumeThreads) * 16;
+  if (bytes % kStep != 0 || bytes > kStep * kConsumeMaxVecs) return MOE_ERR_INVALID_ARG;
+  if (bytes == 0) return MOE_OK;
+  if (src == nullptr || sink == nullptr) return MOE_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(src) % 16 != 0) return MOE_ERR_ALIGNMENT;
+  hipLaunchKernelGGL(probe_consume_kernel, dim3(1), dim3(kConsumeThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src),
+                     static_cast<int>(bytes / kStep), sink);
   return launched();
 }
 

@@ -29,6 +29,10 @@ def load_library():
     lib.moe_probe_write.restype = ctypes.c_int
     lib.moe_probe_gather.argtypes = [p, p, i64, i32, i64, p, p]
     lib.moe_probe_gather.restype = ctypes.c_int
+    lib.moe_probe_empty.argtypes = [i32, p]
+    lib.moe_probe_empty.restype = ctypes.c_int
+    lib.moe_probe_consume.argtypes = [p, sz, p, p]
+    lib.moe_probe_consume.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -59,3 +63,18 @@ def gather(rows: torch.Tensor, restore: torch.Tensor, T: int, K: int, sink: torc
                                          rows.shape[1] * rows.element_size(), _ptr(sink),
                                          _stream(stream, rows))
     _check("moe_probe_gather", st)
+
+
+def empty(workgroups: int = 1, stream=None):
+    """A launch of `workgroups` workgroups that do nothing."""
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    st = load_library().moe_probe_empty(int(workgroups), _stream(stream))
+    _check("moe_probe_empty", st)
+
+
+def consume(src: torch.Tensor, sink: torch.Tensor, stream=None):
+    """One workgroup reads every byte of src (at most 256 KiB)."""
+    st = load_library().moe_probe_consume(_ptr(src), src.numel() * src.element_size(),
+                                          _ptr(sink), _stream(stream, src))
+    _check("moe_probe_consume", st)

@@ -59,7 +59,8 @@ def probe_lib():
 def test_probe_library_exports_its_header(probe_lib):
     src = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(moe_probe_\w+)\s*\(", src)))
-    assert names == ["moe_probe_gather", "moe_probe_read", "moe_probe_write"]
+    assert names == ["moe_probe_consume", "moe_probe_empty", "moe_probe_gather", "moe_probe_read",
+                     "moe_probe_write"]
     for fn in names:
         assert hasattr(probe_lib, fn), fn
 
@@ -76,6 +77,13 @@ def test_probe_validation(probe_lib):
     assert probe_lib.moe_probe_gather(FAKE, FAKE, -1, 8, 14336, FAKE, None) == INVALID
     assert probe_lib.moe_probe_gather(FAKE, FAKE, 4, 0, 14336, FAKE, None) == INVALID
     assert probe_lib.moe_probe_gather(FAKE, FAKE, 4, 8, 14330, FAKE, None) == INVALID
+    assert probe_lib.moe_probe_empty(0, None) == INVALID
+    assert probe_lib.moe_probe_empty(65536, None) == INVALID
+    assert probe_lib.moe_probe_consume(FAKE, 16384 + 16, FAKE, None) == INVALID
+    assert probe_lib.moe_probe_consume(FAKE, 17 * 16384, FAKE, None) == INVALID
+    assert probe_lib.moe_probe_consume(None, 16384, FAKE, None) == INVALID
+    assert probe_lib.moe_probe_consume(FAKE_ODD, 16384, FAKE, None) == ALIGNMENT
+    assert probe_lib.moe_probe_consume(None, 0, None, None) == OK
     assert probe_lib.moe_probe_gather(FAKE_ODD, FAKE, 4, 8, 14336, FAKE, None) == ALIGNMENT
     assert probe_lib.moe_probe_gather(None, None, 0, 8, 14336, None, None) == OK
 
