@@ -55,15 +55,6 @@ def encode(t: torch.Tensor):
     return bf16_bits(t), oracle_code(t.dtype)
 
 
-def assert_16bit_within_one_ulp(got_bits, exp_bits, what):
-    g = _bf16_ordered(np.asarray(got_bits, np.uint16))
-    e = _bf16_ordered(np.asarray(exp_bits, np.uint16))
-    d = np.abs(g - e)
-    if d.max(initial=0) > 1:
-        i = np.argwhere(d > 1)[:5]
-        raise AssertionError("%s more than 1 ulp off at %s" % (what, i.tolist()))
-
-
 def gpu_router(scores, bias, K, G, TG, norm, scale, mode=0):
     """Router on the GPU; weights come back as a host tensor in the scores'
     dtype (numpy float32 for fp32 scores)."""

@@ -8,7 +8,7 @@ import os
 import re
 
 import pytest
-import torch  # noqa: F401  (the binding must share torch's HIP runtime)
+import torch  # the binding must share torch's HIP runtime
 
 from permutation_group_limited_amd import binding
 
@@ -314,3 +314,30 @@ def test_route_and_index_binding_rejects_host_tensors(lib):
                                     z(9, dtype=torch.int32), z(8, dtype=torch.int32),
                                     z(8, dtype=torch.int32), z(2, dtype=torch.int32), z(4, 8),
                                     z(8), z(1, dtype=torch.int32), 1, 1, True, 1.0)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the HIP library there is no other path: the loader and every
+    entry point raise before touching any tensor (nothing falls back to the
+    CPU or to the oracle)."""
+    from permutation_group_limited_amd import binding, probe
+    monkeypatch.setattr(binding, "_LIB_PATH", str(tmp_path / "absent.so"))
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        binding.load_library()
+    x = torch.zeros(4, 8)
+    calls = [
+        lambda: binding.moe_finalize(x, torch.zeros(8, 8), torch.zeros(8, dtype=torch.int32),
+                                     torch.zeros(4, 2)),
+        lambda: binding.moe_router_group_limited(torch.zeros(4, 2, dtype=torch.int32),
+                                                 torch.zeros(4, 2), x, torch.zeros(8), 1, 1,
+                                                 True, 1.0),
+        lambda: binding.moe_create_indices_workspace_size(8, 8),
+    ]
+    for call in calls:
+        with pytest.raises(RuntimeError, match="not built"):
+            call()
+    monkeypatch.setattr(probe, "_LIB_PATH", str(tmp_path / "absent_probe.so"))
+    monkeypatch.setattr(probe, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        probe.load_library()
