@@ -24,9 +24,10 @@ Reported beside the throughput:
     by its mean duration above, against 8 TB/s; plus the HBM bytes measured
     by rocprofv3 counters when the committed counter summary matches the
     current kernel source;
-  * protocol: the step and each stage captured in HIP graphs, replayed with
-    a cold cache (1 GiB read before each replay, outside the events) and
-    warm, median / minimum;
+  * protocol: the step and each stage captured in HIP graphs (one per
+    output buffer, replayed in turn), replayed with a cold cache (1 GiB
+    written before each replay, outside the events; a 1 GiB read instead
+    reported beside it) and warm, median / minimum;
   * extras.configs: all five workloads (tiny, mixtral, dsv3, decode, skewed)
     with 20 steps per HIP graph: GPU time per step, per stage, algorithmic
     bandwidth and fraction of 8 TB/s, finalize's fraction, and parity of
@@ -287,10 +288,7 @@ def main():
 
     if not args.no_extras:
         reps = 20 if N * wk.H > (1 << 31) else 100
-        result["protocol"] = timing_protocol(
-            P.step, {"router": P.router, "create_indices": P.indices,
-                     "route_and_index": P.route_and_index, "finalize": P.finalize},
-            replays=reps)
+        result["protocol"] = timing_protocol(P, replays=reps)
         P.route_and_index()
         torch.cuda.synchronize()
         ex = {}
@@ -452,7 +450,7 @@ def probes(P, steps):
     """Rates of finalize's own access patterns on their own, at the headline
     shape (libmoe_probe.so): a streaming read of `down` (8 KiB per wave of
     non-temporal 16-byte loads), a 1 GiB streaming read, the output written
-    alone (16-byte sc1 stores) into the rotating output buffers, and the
+    alone (finalize's 16-byte stores) into the rotating output buffers, and the
     gather of finalize without its stores. read-phase + write-phase is what
     finalize would take if its reads and writes did not share the memory at
     the same time."""
@@ -468,8 +466,12 @@ def probes(P, steps):
     out_bytes = T * H * P.outs[0].element_size()
     k = [0]
 
+    # finalize streams its output (nt stores) when its gathered rows exceed
+    # the 256 MiB memory-side cache, and keeps it there (sc1) otherwise
+    streaming = down_bytes > (256 << 20)
+
     def write_next():
-        probe.write(P.outs[k[0] % len(P.outs)])
+        probe.write(P.outs[k[0] % len(P.outs)], streaming=streaming)
         k[0] += 1
 
     for f in (lambda: probe.read(big, sink), lambda: probe.read(P.down, sink), write_next,
@@ -613,18 +615,34 @@ def two_batches_in_flight(P, steps):
             "token_slots_per_s_two_streams": N / (two * 1e-6), "outputs_equal": bool(same)}
 
 
-def timing_protocol(step, stages, flush_bytes=1 << 30, replays=100):
-    """The step and each stage captured in HIP graphs and replayed (one step
-    per graph, and 20 steps per graph for the GPU time per step with the
-    graph launch amortised): `replays` times with a cold cache (a read of
-    flush_bytes from a scratch buffer before each replay, outside the timed
-    events: more than the 256 MB memory-side cache and the L2s together; a
-    read, so that no write-back of the flush itself overlaps the replay)
-    and as many times warm; median and minimum in microseconds. Also a plain
-    device copy of flush_bytes (read + write bytes / time)."""
+def timing_protocol(P, flush_bytes=1 << 30, replays=100):
+    """The step and each stage captured in HIP graphs and replayed. Output
+    buffers rotate as in the eager loop: one graph per output buffer,
+    replayed in turn (a graph that rewrote one buffer would find part of
+    its previous output still in the memory-side cache). Cold: flush_bytes
+    written to a scratch buffer before each replay, outside the timed
+    events (more than the 256 MB memory-side cache and the L2s together,
+    which it leaves full of dirty lines, as the kernels before a step
+    would); the same with a read of flush_bytes instead is reported beside
+    it ("read_flush": a clean cache then absorbs the replay's stores and
+    writes them back after the timed events). Warm: no flush. Median and
+    minimum in microseconds; 20 steps per graph for the GPU time per step
+    with the graph launch amortised; and a plain device copy of
+    flush_bytes (read + write bytes / time)."""
     import torch
     scratch = torch.ones(flush_bytes // 8, dtype=torch.int64, device="cuda:0")
     sink = torch.empty((), dtype=torch.int64, device="cuda:0")
+
+    def finalize_into(k):
+        return lambda: P.b.moe_finalize(P.outs[k], P.down, P.restore, P.wts)
+
+    def step_into(k):
+        fin = finalize_into(k)
+
+        def step():
+            P.route_and_index()
+            fin()
+        return step
 
     def capture(fn):
         st = torch.cuda.Stream()
@@ -641,35 +659,49 @@ def timing_protocol(step, stages, flush_bytes=1 << 30, replays=100):
         torch.cuda.synchronize()
         return g
 
-    def replay_times(g, cold):
+    def replay_times(graphs, flush):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(replays)]
-        for a, b in evs:
-            if cold:
+        for i, (a, b) in enumerate(evs):
+            if flush == "write":
+                scratch.fill_(i)
+            elif flush == "read":
                 torch.sum(scratch, dim=0, out=sink)
             a.record()
-            g.replay()
+            graphs[i % len(graphs)].replay()
             b.record()
         torch.cuda.synchronize()
         us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
         return {"median_us": us[len(us) // 2], "min_us": us[0], "replays": replays}
 
-    res = {}
-    g = capture(step)
-    res["step_graph_cold"] = replay_times(g, True)
-    res["step_graph_warm"] = replay_times(g, False)
+    n_out = len(P.outs)
+    res = {"outputs": "one graph per output buffer (%d), replayed in turn" % n_out,
+           "cold_flush": "%d-byte write before each replay" % flush_bytes}
+    graphs = [capture(step_into(k)) for k in range(n_out)]
+    res["step_graph_cold"] = replay_times(graphs, "write")
+    res["step_graph_cold_read_flush"] = replay_times(graphs, "read")
+    res["step_graph_warm"] = replay_times(graphs, None)
+    del graphs
     many = 20
 
     def steps():
-        for _ in range(many):
-            step()
+        for i in range(many):
+            step_into(i % n_out)()
 
-    g20 = capture(steps)
-    w20 = replay_times(g20, False)
+    w20 = replay_times([capture(steps)], None)
     res["steps_per_graph_20_warm_us_per_step"] = {"median": w20["median_us"] / many,
                                                    "min": w20["min_us"] / many}
-    res["stage_graph_cold_median_us"] = {
-        name: replay_times(capture(fn), True)["median_us"] for name, fn in stages.items()}
+    stages = {"router": [P.router], "create_indices": [P.indices],
+              "route_and_index": [P.route_and_index],
+              "finalize": [finalize_into(k) for k in range(n_out)]}
+    res["stage_graph_cold_median_us"] = {}
+    res["stage_graph_cold_read_flush_median_us"] = {}
+    for name, fns in stages.items():
+        graphs = [capture(fn) for fn in fns]
+        res["stage_graph_cold_median_us"][name] = replay_times(graphs, "write")["median_us"]
+        res["stage_graph_cold_read_flush_median_us"][name] = \
+            replay_times(graphs, "read")["median_us"]
+        del graphs
     dst = torch.empty_like(scratch)
     dst.copy_(scratch)
     torch.cuda.synchronize()

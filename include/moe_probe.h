@@ -39,12 +39,15 @@ moe_status_t moe_probe_read(const void* src, size_t bytes, uint32_t* sink, void*
 /*
  * moe_probe_write
  * Fills `bytes` bytes of `dst` with the 32-bit `value`: each wave writes
- * 1 KiB as one 16-byte store per lane through a buffer resource with cache
- * policy sc1 (the stores of moe_finalize).
+ * 1 KiB as one 16-byte store per lane through a buffer resource, with cache
+ * policy nt when `streaming` is non-zero and sc1 otherwise (the two kinds of
+ * store moe_finalize makes: nt when its gathered rows exceed the 256 MiB
+ * memory-side cache, sc1 below).
  * Validation: bytes a multiple of 1024 and at most 2^40; dst 16-byte
  * aligned and non-NULL when bytes > 0.
  */
-moe_status_t moe_probe_write(void* dst, size_t bytes, uint32_t value, void* stream);
+moe_status_t moe_probe_write(void* dst, size_t bytes, uint32_t value, int32_t streaming,
+                             void* stream);
 
 /*
  * moe_probe_gather

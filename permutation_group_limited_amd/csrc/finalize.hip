@@ -36,15 +36,23 @@ __device__ __forceinline__ void widen16(const u32x4& v, float* f) {
 }
 
 // Output stores go through a buffer resource spanning the token's output
-// row, with cache policy sc1: on the DSv3-shaped gather that ran 3-4% faster
-// than default or non-temporal stores (measured; the loads stay
-// non-temporal, which matters far more).
-constexpr int kStorePolicy = 16;         // cache-policy operand: sc1
+// row. Their cache policy depends on the problem's size (the loads stay
+// non-temporal, which matters far more):
+//  * gathered rows that fit the memory-side cache (MI355X: 256 MiB): sc1,
+//    which keeps the output there (Mixtral-shaped, 64 MiB of rows: 15.1 us
+//    against 16.5-17.8 with non-temporal stores, call after call);
+//  * larger: non-temporal, which streams the output out instead of pushing
+//    other lines out of the cache it cannot stay in anyway (DSv3-shaped,
+//    0.94 GB of rows: 182.7 against 185.5 us call after call, and 187 against
+//    195.6 us with the cache full of other data before each call).
+constexpr int kStoreKeep = 16;         // cache-policy operand: sc1
+constexpr int kStoreStream = 2;        // cache-policy operand: nt
+constexpr int64_t kMemorySideCacheBytes = int64_t{256} << 20;
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
 
 // Store VEC fp32 accumulators as D at byte offset `off` of the row (VEC *
-// kBytes bytes, one or two vector stores).
-template <typename D, int VEC>
+// kBytes bytes, one or two vector stores) with cache policy POL.
+template <typename D, int VEC, int POL>
 __device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t row, uint32_t off,
                                           const float* acc) {
   if constexpr (D::kBytes == 4) {
@@ -55,8 +63,7 @@ __device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t row, uint32_t o
       v.y = D::narrow_bits(acc[q + 1]);
       v.z = D::narrow_bits(acc[q + 2]);
       v.w = D::narrow_bits(acc[q + 3]);
-      __builtin_amdgcn_raw_buffer_store_b128(v, row, static_cast<int>(off + q * 4), 0,
-                                             kStorePolicy);
+      __builtin_amdgcn_raw_buffer_store_b128(v, row, static_cast<int>(off + q * 4), 0, POL);
     }
   } else if constexpr (VEC == 8) {
     u32x4 v;
@@ -64,12 +71,12 @@ __device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t row, uint32_t o
     v.y = D::narrow_bits(acc[2]) | (D::narrow_bits(acc[3]) << 16);
     v.z = D::narrow_bits(acc[4]) | (D::narrow_bits(acc[5]) << 16);
     v.w = D::narrow_bits(acc[6]) | (D::narrow_bits(acc[7]) << 16);
-    __builtin_amdgcn_raw_buffer_store_b128(v, row, static_cast<int>(off), 0, kStorePolicy);
+    __builtin_amdgcn_raw_buffer_store_b128(v, row, static_cast<int>(off), 0, POL);
   } else {
     u32x2 v;
     v.x = D::narrow_bits(acc[0]) | (D::narrow_bits(acc[1]) << 16);
     v.y = D::narrow_bits(acc[2]) | (D::narrow_bits(acc[3]) << 16);
-    __builtin_amdgcn_raw_buffer_store_b64(v, row, static_cast<int>(off), 0, kStorePolicy);
+    __builtin_amdgcn_raw_buffer_store_b64(v, row, static_cast<int>(off), 0, POL);
   }
 }
 
@@ -80,7 +87,7 @@ template <typename DD, typename DO, int KB, bool EXACT>
 __global__ __launch_bounds__(kBlock) void finalize_kernel(
     typename DO::storage* __restrict__ out, const typename DD::storage* __restrict__ down,
     const uint32_t* __restrict__ restore, const void* __restrict__ weight, moe_dtype_t wd,
-    int64_t T, int32_t K, int64_t H, int32_t chunks_per_row, uint32_t n_rows) {
+    int64_t T, int32_t K, int64_t H, int32_t chunks_per_row, uint32_t n_rows, int32_t stream_out) {
   constexpr int VEC = 16 / DD::kBytes;  // elements per 16-byte load
   const int lane = lane_id();
   // the host keeps T * chunks_per_row below 2^32, so 32-bit scalar math;
@@ -141,7 +148,10 @@ __global__ __launch_bounds__(kBlock) void finalize_kernel(
   constexpr int64_t kOutBytes = sizeof(typename DO::storage);
   const __amdgpu_buffer_rsrc_t row = __builtin_amdgcn_make_buffer_rsrc(
       out + t * H, 0, static_cast<int>(H * kOutBytes), kRsrcWord3);
-  store_out<DO, VEC>(row, static_cast<uint32_t>(h * kOutBytes), acc);
+  if (stream_out)  // wave-uniform
+    store_out<DO, VEC, kStoreStream>(row, static_cast<uint32_t>(h * kOutBytes), acc);
+  else
+    store_out<DO, VEC, kStoreKeep>(row, static_cast<uint32_t>(h * kOutBytes), acc);
 }
 
 template <typename DD, typename DO>
@@ -161,9 +171,10 @@ moe_status_t launch_typed(void* out, const void* down, const uint32_t* restore,
   const auto* d = static_cast<const typename DD::storage*>(down);
   const dim3 grid = grid_1d(blocks, kBlock), block(kBlock);
   const int32_t c = static_cast<int32_t>(cpr);
+  const int32_t stream_out = T * K * H * DD::kBytes > kMemorySideCacheBytes ? 1 : 0;
 #define MOE_FIN(KB, EXACT)                                                                  \
   hipLaunchKernelGGL((finalize_kernel<DD, DO, KB, EXACT>), grid, block, 0, stream, o, d, \
-                     restore, weight, wd, T, K, H, c, n_rows)
+                     restore, weight, wd, T, K, H, c, n_rows, stream_out)
   switch (K) {
     case 1: MOE_FIN(1, true); break;
     case 2: MOE_FIN(2, true); break;

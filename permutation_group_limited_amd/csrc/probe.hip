@@ -14,7 +14,8 @@ namespace {
 // A data-dependent store that never happens on real data keeps every load
 // live without adding traffic.
 constexpr uint32_t kMagic = 0x9E3779B9u;
-constexpr int kStorePolicy = 16;        // sc1, as finalize's output stores
+constexpr int kStoreKeep = 16;          // sc1 and nt: finalize's two output policies
+constexpr int kStoreStream = 2;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 constexpr int kReadVecsPerLane = 8;     // 8 x 16 B per lane: 8 KiB per wave
 
@@ -41,14 +42,18 @@ __global__ __launch_bounds__(kBlock) void probe_read_kernel(const u32x4* __restr
 }
 
 __global__ __launch_bounds__(kBlock) void probe_write_kernel(uint32_t* __restrict__ dst,
-                                                             uint64_t n_waves, uint32_t value) {
+                                                             uint64_t n_waves, uint32_t value,
+                                                             int32_t streaming) {
   const uint64_t w = wave_index();
   if (w >= n_waves) return;
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc(dst + w * (kWave * 4), 0, kWave * 16, kRsrcWord3);
   u32x4 v;
   v.x = v.y = v.z = v.w = value;
-  __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, lane_id() * 16, 0, kStorePolicy);
+  if (streaming)  // uniform
+    __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, lane_id() * 16, 0, kStoreStream);
+  else
+    __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, lane_id() * 16, 0, kStoreKeep);
 }
 
 // One wave per (token, 64 x 16-byte chunk of the row); rows addressed in 64
@@ -127,7 +132,8 @@ moe_status_t moe_probe_read(const void* src, size_t bytes, uint32_t* sink, void*
   return launched();
 }
 
-moe_status_t moe_probe_write(void* dst, size_t bytes, uint32_t value, void* stream) {
+moe_status_t moe_probe_write(void* dst, size_t bytes, uint32_t value, int32_t streaming,
+                             void* stream) {
   constexpr size_t kWaveBytes = kWave * 16;
   if (bytes % kWaveBytes != 0 || bytes > kMaxProbeBytes) return MOE_ERR_INVALID_ARG;
   if (bytes == 0) return MOE_OK;
@@ -136,7 +142,8 @@ moe_status_t moe_probe_write(void* dst, size_t bytes, uint32_t value, void* stre
   const uint64_t waves = bytes / kWaveBytes;
   const int64_t blocks = static_cast<int64_t>((waves + kWavesPerBlock - 1) / kWavesPerBlock);
   hipLaunchKernelGGL(probe_write_kernel, grid_1d(blocks, kBlock), dim3(kBlock), 0,
-                     static_cast<hipStream_t>(stream), static_cast<uint32_t*>(dst), waves, value);
+                     static_cast<hipStream_t>(stream), static_cast<uint32_t*>(dst), waves, value,
+                     streaming);
   return launched();
 }
 

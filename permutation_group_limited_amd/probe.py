@@ -25,7 +25,7 @@ def load_library():
     p, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.moe_probe_read.argtypes = [p, sz, p, p]
     lib.moe_probe_read.restype = ctypes.c_int
-    lib.moe_probe_write.argtypes = [p, sz, ctypes.c_uint32, p]
+    lib.moe_probe_write.argtypes = [p, sz, ctypes.c_uint32, i32, p]
     lib.moe_probe_write.restype = ctypes.c_int
     lib.moe_probe_gather.argtypes = [p, p, i64, i32, i64, p, p]
     lib.moe_probe_gather.restype = ctypes.c_int
@@ -49,10 +49,12 @@ def read(src: torch.Tensor, sink: torch.Tensor, stream=None):
     _check("moe_probe_read", st)
 
 
-def write(dst: torch.Tensor, value: int = 0x3F803F80, stream=None):
-    """Fill every byte of dst (finalize's stores)."""
+def write(dst: torch.Tensor, value: int = 0x3F803F80, streaming: bool = False, stream=None):
+    """Fill every byte of dst (finalize's stores: non-temporal when
+    `streaming`, sc1 otherwise)."""
     st = load_library().moe_probe_write(_ptr(dst), dst.numel() * dst.element_size(),
-                                        value & 0xFFFFFFFF, _stream(stream, dst))
+                                        value & 0xFFFFFFFF, 1 if streaming else 0,
+                                        _stream(stream, dst))
     _check("moe_probe_write", st)
 
 

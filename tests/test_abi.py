@@ -72,8 +72,8 @@ def test_probe_validation(probe_lib):
     assert probe_lib.moe_probe_read(FAKE_ODD, 8192, FAKE, None) == ALIGNMENT
     assert probe_lib.moe_probe_read(FAKE, (1 << 40) + 8192, FAKE, None) == INVALID
     assert probe_lib.moe_probe_read(None, 0, None, None) == OK
-    assert probe_lib.moe_probe_write(FAKE, 1000, 0, None) == INVALID
-    assert probe_lib.moe_probe_write(FAKE_ODD, 1024, 0, None) == ALIGNMENT
+    assert probe_lib.moe_probe_write(FAKE, 1000, 0, 0, None) == INVALID
+    assert probe_lib.moe_probe_write(FAKE_ODD, 1024, 0, 1, None) == ALIGNMENT
     assert probe_lib.moe_probe_gather(FAKE, FAKE, -1, 8, 14336, FAKE, None) == INVALID
     assert probe_lib.moe_probe_gather(FAKE, FAKE, 4, 0, 14336, FAKE, None) == INVALID
     assert probe_lib.moe_probe_gather(FAKE, FAKE, 4, 8, 14330, FAKE, None) == INVALID
