@@ -156,7 +156,8 @@ def test_overflow_to_infinity(odt):
 # (a mixed-precision fma rounding the exact sum straight to binary16 would
 # differ there). Ragged H (7160: the last 16-byte column of a 512-element
 # chunk missing), long rows (14336, 16384), every K up to 8, all 16-bit
-# dtype combinations.
+# dtype combinations; both output store policies (gathered rows below and
+# above 256 MiB).
 LARGE_CASES = [
     # T, K, H, down, weight, out
     (8200, 8, 7168, "bf16", "f32", "bf16"),
@@ -167,6 +168,10 @@ LARGE_CASES = [
     (8197, 6, 4096, "bf16", "f16", "bf16"),
     (4099, 7, 8192, "bf16", "f32", "f16"),
     (8195, 2, 4096, "f16", "bf16", "bf16"),
+    # fp32 rows past the 256 MiB memory-side cache (non-temporal output
+    # stores): two 16-byte stores per lane, and one 8-byte store
+    (2100, 8, 4096, "f32", "f32", "f32"),
+    (4500, 4, 4096, "f32", "bf16", "bf16"),
 ]
 
 
