@@ -275,11 +275,11 @@ size_t moe_create_indices_no_alloc_max_scratch_bytes(void);
  * per token and E experts: a 256-byte header (a counter word and the status
  * word). When E <= 256 and the batch takes two launches, plus a uint32
  * counts matrix of 64 rows of E' words (E' = E rounded up to a multiple of
- * 4) and min(ceil(T / 16), 32768) scratch rows of E' words (one per router
- * workgroup). Otherwise, when the index step may split the T * K slots into
- * several chunks, plus a counts matrix of 64 rows of E words. Never
- * decreases as T grows. 0 for arguments out of range. Pure host
- * computation.
+ * 4) and min(ceil(T / 4), 32768) scratch rows of E' words (one per router
+ * workgroup, which routes at least 4 tokens). Otherwise, when the index
+ * step may split the T * K slots into several chunks, plus a counts matrix
+ * of 64 rows of E words. Never decreases as T grows. 0 for arguments out
+ * of range. Pure host computation.
  */
 size_t moe_route_and_index_workspace_size(int64_t T, int32_t K, int32_t E);
 

@@ -341,3 +341,15 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(probe, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         probe.load_library()
+
+
+def test_route_and_index_workspace_formula():
+    """The header's size formula, ranked form (E <= 256, two launches):
+    256-byte header + 64 count rows + min(ceil(T / 4), 32768) fine rows, of
+    E rounded up to 4 words each."""
+    def expected(T, E):
+        e4 = (E + 3) // 4 * 4
+        return 256 + 64 * e4 * 4 + min((T + 3) // 4, 32768) * e4 * 4
+    for T, K, E in ((8192, 8, 256), (8200, 8, 256), (65536, 8, 256), (4096, 2, 8),
+                    (1 << 20, 8, 256), (3000, 6, 64)):
+        assert binding.moe_route_and_index_workspace_size(T, K, E) == expected(T, E), (T, K, E)
