@@ -68,7 +68,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv3")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time for the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
@@ -750,7 +750,7 @@ def cpu_leg(P, out, budget_s):
         oracle_step()
         steps += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or steps >= 200:
+        if el >= budget_s or steps >= 400:
             break
     baseline = {"value": N * steps / el, "unit": "token-slots/s", "cores": oracle.num_threads(),
                 "kind": "oracle",
