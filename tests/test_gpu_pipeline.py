@@ -119,3 +119,61 @@ def test_graph_replay_of_the_chain(name):
             same = torch.equal(t.view(torch.int16), e.view(torch.int16)) if t.element_size() == 2 \
                 else torch.equal(t.view(torch.int32), e.view(torch.int32))
             assert same, "replay %d: %s differs from the eager chain" % (rep, key)
+
+
+@pytest.mark.parametrize("T", [2048, 8192])
+def test_two_streams_in_flight(T):
+    """Two batches with their own inputs, buffers and workspaces, their steps
+    (route_and_index, then finalize) queued alternately on two streams with
+    no synchronisation in between, five steps each: every step's outputs
+    equal those of the same step run alone, bit for bit, and both
+    workspaces end zero (the ranked form: several index chunks)."""
+    from dataclasses import replace
+    base = wl.WORKLOADS["dsv3"]
+    wks = [replace(base, T=T, seed=11), replace(base, T=T, seed=12)]
+    log("two streams in flight", T)
+
+    def setup(wk):
+        E, K = wk.E, wk.K
+        i32 = lambda *shape: torch.empty(shape, dtype=torch.int32, device=DEV)  # noqa: E731
+        return {"s": wl.make_scores(wk).to(DEV), "b": wl.make_bias(wk).to(DEV),
+                "down": wl.make_down(wk, device=DEV),
+                "idx": i32(T, K), "w": torch.empty(T, K, device=DEV), "order": i32(T * K),
+                "restore": i32(T * K), "starts": i32(E + 1), "eids": i32(E), "stats": i32(2),
+                "ws": torch.zeros(binding.moe_route_and_index_workspace_size(T, K, E) // 4,
+                                  dtype=torch.int32, device=DEV),
+                "out": torch.empty(T, wk.H, dtype=wk.out_dtype, device=DEV)}
+
+    def step(wk, b, stream=None):
+        binding.moe_route_and_index(b["idx"], b["w"], b["order"], b["starts"], b["restore"],
+                                    b["eids"], b["stats"], b["s"], b["b"], b["ws"],
+                                    wk.n_groups, wk.topk_group, wk.norm_weights, wk.scale,
+                                    stream=stream)
+        binding.moe_finalize(b["out"], b["down"], b["restore"], b["w"], stream=stream)
+
+    keys = ("idx", "w", "order", "restore", "starts", "eids", "stats", "out")
+    sets = [setup(wk) for wk in wks]
+    alone = []
+    for wk, b in zip(wks, sets):
+        step(wk, b)
+        torch.cuda.synchronize()
+        alone.append({k: b[k].clone() for k in keys})
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    got = [[], []]
+    for it in range(5):
+        for j in (0, 1):
+            with torch.cuda.stream(streams[j]):
+                step(wks[j], sets[j], stream=streams[j])
+                got[j].append({k: sets[j][k].clone() for k in keys})
+    torch.cuda.synchronize()
+    for j in (0, 1):
+        assert int(torch.count_nonzero(sets[j]["ws"][:(256 + 64 * wks[j].E * 4) // 4])) == 0
+        for it, g in enumerate(got[j]):
+            for k in keys:
+                a, e = g[k], alone[j][k]
+                same = torch.equal(a.view(torch.int16), e.view(torch.int16)) \
+                    if a.element_size() == 2 else torch.equal(a.view(torch.int32),
+                                                              e.view(torch.int32))
+                assert same, "stream %d step %d: %s differs from the step run alone" % (j, it, k)
