@@ -7,12 +7,14 @@
 //
 // HBM-bound streaming gather. Mapping: one wave64 per (token, 64 x 16-byte
 // column chunk of the row). The wave's token is uniform, so its K restore
-// entries and K weights come in through scalar loads; each lane then issues
-// K independent 16-byte non-temporal loads (one per gathered row, all in
-// flight together; every row segment is read exactly once), folds them with
-// one fmaf per element in ascending k, and writes its output slice with one
-// 16-byte buffer store (cache policy below). Rows of `down` are addressed in
-// 64 bits (T*K*H elements exceed 2^32 for large prefill batches).
+// entries (and fp32 weights) come in through scalar loads; each lane then
+// issues K independent 16-byte non-temporal loads (one per gathered row,
+// all in flight together; every row segment is read exactly once), folds
+// them with one fmaf per element in ascending k, and writes its output
+// slice with buffer stores (one 16-byte store, two for fp32 output, one
+// 8-byte store for fp32 rows into 16-bit output; cache policy below). Rows
+// of `down` are addressed in 64 bits (T*K*H elements exceed 2^32 for large
+// prefill batches).
 #include "common.hpp"
 
 namespace moe {
