@@ -757,7 +757,7 @@ def cpu_leg(P, out, budget_s):
                 "sample": "%d whole steps of the %s workload (router + create_indices + "
                           "finalize), %.1f s" % (steps, wk.name, el)}
 
-    # per stage, once each, on all threads and on one thread
+    # per stage, median of 3 runs, on all threads and on one thread
     def stage_times():
         t = {}
         a = time.perf_counter()
@@ -771,13 +771,19 @@ def cpu_leg(P, out, budget_s):
         t["finalize"] = time.perf_counter() - a
         return {k: v * 1e3 for k, v in t.items()}
 
+    def median_stage_times(runs=3):
+        ts = [stage_times() for _ in range(runs)]
+        return {k: sorted(t[k] for t in ts)[runs // 2] for k in ts[0]}
+
     threads = oracle.num_threads()
-    baseline["stage_ms"] = stage_times()
+    baseline["stage_ms"] = median_stage_times()
     oracle.set_num_threads(1)
     try:
-        baseline["single_thread_stage_ms"] = stage_times()
+        baseline["single_thread_stage_ms"] = median_stage_times()
     finally:
         oracle.set_num_threads(threads)
+    baseline["host_cpus"] = {"cpu_count": os.cpu_count(),
+                             "affinity": len(os.sched_getaffinity(0))}
     return baseline, oracle_parity(P, out)
 
 
