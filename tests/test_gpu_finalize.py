@@ -156,8 +156,11 @@ def test_overflow_to_infinity(odt):
 # (a mixed-precision fma rounding the exact sum straight to binary16 would
 # differ there). Ragged H (7160: the last 16-byte column of a 512-element
 # chunk missing), long rows (14336, 16384), every K up to 8, all 16-bit
-# dtype combinations; both output store policies (gathered rows below and
-# above 256 MiB).
+# dtype combinations; both launch shapes (gathered rows below 256 MiB: four
+# waves per workgroup, sc1 output stores; above: one wave per workgroup with
+# the LDS reservation that caps the waves per compute unit, non-temporal
+# stores), the latter at K = 2 (no cap), 3, 4, 5, 6, 7, 8 and 16 (batches
+# of 8 rows).
 LARGE_CASES = [
     # T, K, H, down, weight, out
     (8200, 8, 7168, "bf16", "f32", "bf16"),
@@ -172,6 +175,11 @@ LARGE_CASES = [
     # stores): two 16-byte stores per lane, and one 8-byte store
     (2100, 8, 4096, "f32", "f32", "f32"),
     (4500, 4, 4096, "f32", "bf16", "bf16"),
+    # more streaming shapes: K above 8, K = 2 and 3, a ragged last chunk
+    (1100, 16, 8192, "bf16", "f32", "bf16"),
+    (8200, 2, 8192, "bf16", "bf16", "bf16"),
+    (5000, 3, 9216, "f16", "f32", "f16"),
+    (4097, 8, 4104, "bf16", "f32", "bf16"),
 ]
 
 
