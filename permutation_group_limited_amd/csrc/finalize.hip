@@ -27,8 +27,6 @@
 // DeepSeek-V3 shape (T = 8192, K = 8, H = 7168, bf16), 183 -> 173 us
 // call after call and 187 -> 176 us after a 1 GiB write, and at T = 65536
 // 1517 -> 1400 us.
-#include <atomic>
-
 #include "common.hpp"
 
 namespace moe {
@@ -181,31 +179,16 @@ int streaming_wave_cap(int32_t K) {
   return cap >= 32 ? 0 : cap;
 }
 
-// LDS bytes per compute unit of the current device (queried once per device).
-constexpr int kMaxDevices = 64;
-std::atomic<int> g_lds_per_cu[kMaxDevices];
-
-int lds_per_cu() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
-  int v = g_lds_per_cu[dev].load(std::memory_order_relaxed);
-  if (v == 0) {
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
-        hipSuccess)
-      return 0;
-    g_lds_per_cu[dev].store(v, std::memory_order_relaxed);
-  }
-  return v;
-}
+// LDS of one gfx950 compute unit (the only target this library is built
+// for).
+constexpr int kLdsPerCu = 160 * 1024;
 
 // Dynamic LDS for each one-wave workgroup so that at most `cap` of them fit
-// on a compute unit (rounded down to the 512-byte allocation unit); 0 when
-// the cap cannot be expressed within one workgroup's LDS limit.
+// on a compute unit (rounded down to the 512-byte allocation unit); 0 = no
+// cap.
 size_t occupancy_lds_bytes(int cap) {
-  const int per_cu = lds_per_cu();
-  if (cap <= 0 || per_cu <= 0) return 0;
-  const int bytes = (per_cu / cap) / 512 * 512;
-  return bytes > 0 && bytes <= 65536 ? static_cast<size_t>(bytes) : 0;
+  if (cap <= 0) return 0;
+  return static_cast<size_t>((kLdsPerCu / cap) / 512 * 512);
 }
 
 template <typename DD, typename DO>

@@ -258,12 +258,12 @@ def test_back_to_back_calls_share_the_counter():
 
 
 @pytest.mark.parametrize("name,T", [("tiny", None), ("decode", 16), ("decode", None),
-                                    ("dsv3", None)])
+                                    ("mixtral", None), ("dsv3", None)])
 def test_graph_replay(name, T):
     """Captured once, replayed several times with eager work in between;
     every replay gives the eager result and leaves the workspace zero (the
     one-launch form at T = 64, E = 8 and T = 16, E = 256, the two-launch
-    form with one chunk and with several)."""
+    form with one chunk and with several, at E = 8 and E = 256)."""
     wk = wl.WORKLOADS[name]
     if T is not None:
         wk = replace(wk, T=T)
