@@ -199,7 +199,10 @@ moe_status_t launch_typed(void* out, const void* down, const uint32_t* restore,
   const int64_t per_wave = static_cast<int64_t>(kWave) * VEC;
   const int64_t cpr = (H + per_wave - 1) / per_wave;
   const int64_t waves = T * cpr;
-  const int32_t stream_out = T * K * H * DD::kBytes > kMemorySideCacheBytes ? 1 : 0;
+  // gathered rows above the memory-side cache: T * K rows of H * kBytes bytes
+  // (compared by division, so no product can overflow)
+  const int32_t stream_out =
+      T * K > kMemorySideCacheBytes / (H * static_cast<int64_t>(DD::kBytes)) ? 1 : 0;
   const int wpb = stream_out ? 1 : kWavesPerBlock;
   // wave indices (grid padding included) stay below 2^32
   if (waves > 0xFFFFFFFFll - static_cast<int64_t>(kGridRow) * wpb) return MOE_ERR_UNSUPPORTED;
