@@ -22,11 +22,11 @@
 // the compute unit's LDS that it never touches, so that only a few waves
 // share a compute unit: about 64 KiB of row loads in flight per compute unit
 // (9 waves at K = 8, 17 at K = 4; K = 2 is left uncapped). With every wave
-// resident (24 per compute unit at K = 8) the memory queues stay full of
-// reads and the output stream waits behind them; measured at the
-// DeepSeek-V3 shape (T = 8192, K = 8, H = 7168, bf16), 183 -> 173 us
-// call after call and 187 -> 176 us after a 1 GiB write, and at T = 65536
-// 1517 -> 1400 us.
+// resident (24 per compute unit at K = 8) the kernel was slower, while the
+// same gather without its stores was not: the extra reads in flight cost
+// the output stream. Measured at the DeepSeek-V3 shape (T = 8192, K = 8,
+// H = 7168, bf16): 183 -> 173 us call after call and 187 -> 176 us after a
+// 1 GiB write; at T = 65536, 1517 -> 1400 us.
 #include "common.hpp"
 
 namespace moe {
