@@ -204,8 +204,10 @@ moe_status_t launch_typed(void* out, const void* down, const uint32_t* restore,
   const int32_t stream_out =
       T * K > kMemorySideCacheBytes / (H * static_cast<int64_t>(DD::kBytes)) ? 1 : 0;
   const int wpb = stream_out ? 1 : kWavesPerBlock;
-  // wave indices (grid padding included) stay below 2^32
-  if (waves > 0xFFFFFFFFll - static_cast<int64_t>(kGridRow) * wpb) return MOE_ERR_UNSUPPORTED;
+  // wave indices (grid padding included) stay below 2^32; one documented
+  // limit for both launch shapes (the four-wave one needs it)
+  if (waves > 0xFFFFFFFFll - static_cast<int64_t>(kGridRow) * kWavesPerBlock)
+    return MOE_ERR_UNSUPPORTED;
   const int64_t blocks = (waves + wpb - 1) / wpb;
   const size_t lds = stream_out ? occupancy_lds_bytes(streaming_wave_cap(K)) : 0;
   const uint32_t n_rows = static_cast<uint32_t>(T * K);

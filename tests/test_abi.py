@@ -218,8 +218,12 @@ def finalize(lib, T=4, K=2, H=64, od=1, dd=1, wd=0, ptrs=None):
     # output rows of 2^31 bytes or more are not supported
     (dict(H=1 << 29, od=0), UNSUPPORTED), (dict(H=1 << 30, od=1), UNSUPPORTED),
     (dict(H=1 << 40), UNSUPPORTED),
-    # more than 2^32 - 2^18 waves (one per token and 1 KiB of the row)
+    # more than 2^32 - 2^18 waves (one per token and 1 KiB of the row), in
+    # both launch shapes: rows past the memory-side cache (these) take
+    # one-wave workgroups, and the limit is the same just past it
     (dict(T=(1 << 32) - 2, K=1, H=8), UNSUPPORTED),
+    (dict(T=(1 << 32) - (1 << 18), K=1, H=8), UNSUPPORTED),
+    (dict(T=(1 << 32) - (1 << 17), K=1, H=8), UNSUPPORTED),
     (dict(T=1 << 31, K=1, H=1024), UNSUPPORTED),
 ])
 def test_finalize_validation(lib, kw, code):
