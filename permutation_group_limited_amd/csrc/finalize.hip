@@ -185,10 +185,13 @@ constexpr int kLdsPerCu = 160 * 1024;
 
 // Dynamic LDS for each one-wave workgroup so that at most `cap` of them fit
 // on a compute unit (rounded down to the 512-byte allocation unit); 0 = no
-// cap.
+// cap, and no cap either where a workgroup would need more than the 64 KiB
+// it may take without a launch attribute (caps below 3; the caps in use are
+// 9 and up).
 size_t occupancy_lds_bytes(int cap) {
   if (cap <= 0) return 0;
-  return static_cast<size_t>((kLdsPerCu / cap) / 512 * 512);
+  const int bytes = (kLdsPerCu / cap) / 512 * 512;
+  return bytes <= 64 * 1024 ? static_cast<size_t>(bytes) : 0;
 }
 
 template <typename DD, typename DO>
